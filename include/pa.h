@@ -1,0 +1,208 @@
+/*
+ * pa.h -- attention over a block-paged KV cache on AMD Instinct MI355X
+ * (gfx950).  C ABI of libpa.so.
+ *
+ * The operations are the ones an LLM inference engine runs in every
+ * attention layer (nano-vllm deep dive, Step 4 "Attention -- Triton Kernel +
+ * Flash Attention"): write this step's K/V rows into the paged cache, then
+ * run causal attention for a packed prefill batch or for one decode token per
+ * sequence, reading keys and values through a per-sequence block table.
+ *
+ * Conventions for every call
+ *  - Pointers are DEVICE pointers unless marked (host).  Buffers are owned by
+ *    the caller and must stay alive until the work enqueued on `stream`
+ *    completes.  `stream` is a hipStream_t (NULL = the default stream).
+ *  - Calls only enqueue work on `stream`: no device synchronisation, no
+ *    device-to-host copy, no allocation, no global mutable state.  They may
+ *    be called from several host threads and captured in a HIP graph.
+ *  - Errors: a pa_status is returned synchronously for problems visible on
+ *    the host (null pointers, sizes, unsupported shapes, a workspace that is
+ *    too small) and nothing is enqueued.  PA_ERR_HIP means a launch failed
+ *    (hipGetLastError; no synchronisation).  The CONTENTS of device index
+ *    arrays are preconditions that the hot path does not check on the host
+ *    (checking them would need a sync): pa_validate_prefill_metadata and
+ *    pa_validate_decode_metadata check host copies.  The kernels still never
+ *    read a block-table entry past a sequence's last needed block, skip
+ *    block ids outside [0, num_blocks) and slots outside the pool, so bad
+ *    contents give wrong numbers, not out-of-bounds accesses of the pools.
+ *  - No C++ exception crosses this interface.
+ *
+ * KV pool layout (nano-vllm deep dive, Step 5, "KV Cache memory layout"):
+ * one K pool and one V pool per layer, each a contiguous
+ *     [num_blocks][block_size][num_kv_heads][head_dim]
+ * array of `dtype` elements.  Token j of a sequence lives in physical block
+ * block_table[s][j / block_size] at offset j % block_size (same page,
+ * Step 1, "why block_table"); its flat slot is block * block_size + offset.
+ *
+ * Supported: dtype PA_F32 or PA_BF16; head_dim 32, 64, 128 or 256;
+ * block_size a power of two (1 .. 65536); num_q_heads a multiple of
+ * num_kv_heads with group size num_q_heads / num_kv_heads in {1, 2, 4, 8}.
+ * Query head h reads KV head h / (num_q_heads / num_kv_heads).
+ * The bf16 prefill runs on MFMA for head_dim 64 and 128; every other
+ * supported shape runs on the vector ALU path.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PA_ABI_VERSION 1
+
+typedef enum {
+    PA_OK = 0,
+    PA_ERR_NULL_ARG = 1,     /* a required pointer is NULL                      */
+    PA_ERR_BAD_SHAPE = 2,    /* a size or stride is negative or inconsistent    */
+    PA_ERR_BAD_DTYPE = 3,    /* dtype is not PA_F32 / PA_BF16                   */
+    PA_ERR_UNSUPPORTED = 4,  /* head_dim, block_size or group size not built    */
+    PA_ERR_WORKSPACE = 5,    /* workspace NULL or smaller than the *_bytes call */
+    PA_ERR_HIP = 6,          /* a kernel launch failed                          */
+    PA_ERR_BAD_METADATA = 7  /* (validators only) host copy of metadata invalid */
+} pa_status;
+
+typedef enum { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
+
+/* Shape of one layer's K pool (the V pool has the same shape). Host struct. */
+typedef struct {
+    int64_t num_blocks;
+    int32_t block_size;
+    int32_t num_kv_heads;
+    int32_t head_dim;
+    int32_t dtype; /* pa_dtype */
+} pa_pool;
+
+/*
+ * pa_store_kv -- scatter this step's K/V rows into the paged pools.
+ * (nano-vllm deep dive, Step 4, "Triton Kernel: write KV Cache", and the
+ * slot_mapping note there: slot = block_table[block] * block_size + offset.)
+ *
+ *   k, v          [num_tokens][num_kv_heads][head_dim] rows, `pool->dtype`;
+ *                 row t starts at element t * k_row_stride (v_row_stride);
+ *                 strides are in elements and >= num_kv_heads * head_dim.
+ *   slot_mapping  int32 [num_tokens]; slot -1 = padding token, skipped.
+ *   k_pool,v_pool the layer's pools (see layout above), written in place.
+ * Row t is copied bit-for-bit to flat slot slot_mapping[t].  Slots must be
+ * unique within one call (precondition).  num_tokens == 0 is a no-op.
+ */
+pa_status pa_store_kv(const void *k, int64_t k_row_stride,
+                      const void *v, int64_t v_row_stride,
+                      const int32_t *slot_mapping, int32_t num_tokens,
+                      void *k_pool, void *v_pool, const pa_pool *pool /* host */,
+                      void *stream);
+
+/*
+ * pa_prefill_varlen -- causal attention for a packed variable-length batch
+ * over the paged cache (nano-vllm deep dive, Step 4, flash_attn_varlen_func
+ * with cu_seqlens_q / cu_seqlens_k / block_table, causal; Step 5,
+ * prepare_prefill: query tokens are the uncached ones, keys are all tokens).
+ *
+ *   q             [total_q][num_q_heads][head_dim], row stride q_row_stride
+ *                 elements (>= num_q_heads * head_dim), `pool->dtype`.
+ *   cu_seqlens_q  int32 [num_seqs + 1], cu_seqlens_q[0] = 0, non-decreasing,
+ *                 cu_seqlens_q[num_seqs] = total_q.  Sequence s owns query
+ *                 rows cu_seqlens_q[s] .. cu_seqlens_q[s+1]-1.
+ *   cu_seqlens_k  int32 [num_seqs + 1]: k_len(s) = cu_seqlens_k[s+1] -
+ *                 cu_seqlens_k[s] keys, ALL already in the pools (call
+ *                 pa_store_kv for the new tokens first, on the same stream).
+ *   q_offsets     int32 [num_seqs]: cached-prefix length of sequence s;
+ *                 query i of s sits at absolute position q_offsets[s] + i
+ *                 and sees keys 0 .. min(q_offsets[s] + i, k_len(s) - 1)
+ *                 (bottom-right causal alignment).  Normally q_offsets[s] +
+ *                 q_len(s) == k_len(s).
+ *   block_table   int32 [num_seqs][block_table_stride] physical block ids;
+ *                 only the first ceil(k_len(s) / block_size) entries of a
+ *                 row are read.
+ *   max_seqlen_q, max_seqlen_k  host upper bounds of q_len(s) and k_len(s)
+ *                 (they size the launch; no device read is needed).
+ *   softmax_scale multiplies q . k before the softmax (usually 1/sqrt(d)).
+ *   out           [total_q][num_q_heads][head_dim] contiguous, `pool->dtype`
+ *                 (bf16 output is rounded to nearest-even).
+ *   workspace     device scratch of at least pa_prefill_workspace_bytes(...)
+ *                 bytes (may be NULL when that returns 0).
+ * Sequences with q_len 0 are no-ops; a query row with no visible key
+ * (k_len 0) gets a zero output.
+ */
+pa_status pa_prefill_varlen(const void *q, int64_t q_row_stride, int32_t num_q_heads,
+                            const void *k_pool, const void *v_pool, const pa_pool *pool /* host */,
+                            const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k,
+                            const int32_t *q_offsets, const int32_t *block_table,
+                            int32_t block_table_stride, int32_t num_seqs, int32_t total_q,
+                            int32_t max_seqlen_q, int32_t max_seqlen_k, float softmax_scale,
+                            void *out, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * pa_decode -- one query token per sequence against its paged context
+ * (nano-vllm deep dive, Step 4, flash_attn_with_kvcache with cache_seqlens
+ * and block_table; Step 5, prepare_decode: context length = len(seq), the
+ * new token included; its K/V must already be stored).
+ *
+ *   q             [num_seqs][num_q_heads][head_dim], row stride q_row_stride.
+ *   context_lens  int32 [num_seqs]; sequence s attends to keys
+ *                 0 .. context_lens[s]-1.  0 marks a padding row (output 0).
+ *   block_table   int32 [num_seqs][block_table_stride].
+ *   max_context_len  host upper bound of context_lens (sizes the launch).
+ *   out           [num_seqs][num_q_heads][head_dim] contiguous.
+ *   workspace     >= pa_decode_workspace_bytes(...) bytes: split-K partial
+ *                 results (running max, normaliser and fp32 accumulator per
+ *                 split), merged by log-sum-exp (fork Q&A, general Q&A,
+ *                 "what is split-K").
+ */
+pa_status pa_decode(const void *q, int64_t q_row_stride, int32_t num_q_heads,
+                    const void *k_pool, const void *v_pool, const pa_pool *pool /* host */,
+                    const int32_t *context_lens, const int32_t *block_table,
+                    int32_t block_table_stride, int32_t num_seqs, int32_t max_context_len,
+                    float softmax_scale, void *out, void *workspace, size_t workspace_bytes,
+                    void *stream);
+
+/* Workspace sizes (bytes) for the matching calls with the same host sizes. */
+size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t total_q, int32_t num_q_heads,
+                                  int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                  const pa_pool *pool /* host */);
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,
+                                 const pa_pool *pool /* host */);
+
+/*
+ * pa_gather_kv -- test and debug helper, not on the hot path: copy every
+ * sequence's keys/values out of the pools, walking the block table, into
+ * packed [total_k][num_kv_heads][head_dim] arrays (row cu_seqlens_k[s] + j
+ * holds key j of sequence s).  Bit-exact.  (mini-infer 03, section 2: the
+ * dense gather that paged attention avoids.)
+ */
+pa_status pa_gather_kv(const void *k_pool, const void *v_pool, const pa_pool *pool /* host */,
+                       const int32_t *cu_seqlens_k, const int32_t *block_table,
+                       int32_t block_table_stride, int32_t num_seqs, int32_t total_k,
+                       void *k_out, void *v_out, void *stream);
+
+/*
+ * Host-side validators of HOST copies of the metadata (never called by the
+ * hot path).  They return PA_OK or PA_ERR_BAD_METADATA / PA_ERR_BAD_SHAPE and
+ * write a short reason into `why` (host buffer of why_len bytes, may be NULL).
+ * Prefill: cu_seqlens monotone from 0, q_len <= k_len, q_offsets[s] + q_len
+ * == k_len, lengths within the maxima and the block table width, block ids of
+ * every needed entry in range.  slot_mapping (may be NULL): ids in range or
+ * -1, no duplicates.  Decode: 0 <= context_lens <= max_context_len, ids in
+ * range.
+ */
+pa_status pa_validate_prefill_metadata(const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k,
+                                       const int32_t *q_offsets, const int32_t *block_table,
+                                       int32_t block_table_stride, int32_t num_seqs,
+                                       int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                       const int32_t *slot_mapping, int32_t num_slots,
+                                       const pa_pool *pool, char *why, size_t why_len);
+pa_status pa_validate_decode_metadata(const int32_t *context_lens, const int32_t *block_table,
+                                      int32_t block_table_stride, int32_t num_seqs,
+                                      int32_t max_context_len, const int32_t *slot_mapping,
+                                      const pa_pool *pool, char *why, size_t why_len);
+
+const char *pa_status_string(pa_status status);
+int pa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

@@ -1,0 +1,297 @@
+// pa_api.cpp -- the extern "C" entry points of libpa (see include/pa.h).
+// Host-side argument checks, launch planning and dispatch.  Nothing here
+// synchronises the device, allocates, or reads device memory.
+#include <hip/hip_runtime.h>
+
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <vector>
+
+#include "pa.h"
+#include "pa_kernels.h"
+
+namespace {
+
+bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+
+int log2i(int64_t x) {
+    int s = 0;
+    while ((int64_t(1) << s) < x) ++s;
+    return s;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+int elem_bytes(int dtype) { return dtype == PA_F32 ? 4 : (dtype == PA_BF16 ? 2 : 0); }
+
+// Checks shared by every call that reads the pools.
+pa_status check_pool(const pa_pool *pool, pa::PoolGeom *g) {
+    if (!pool) return PA_ERR_NULL_ARG;
+    if (!elem_bytes(pool->dtype)) return PA_ERR_BAD_DTYPE;
+    if (pool->num_blocks < 0 || pool->block_size <= 0 || pool->num_kv_heads <= 0 || pool->head_dim <= 0)
+        return PA_ERR_BAD_SHAPE;
+    if (!is_pow2(pool->block_size) || pool->block_size > 65536) return PA_ERR_UNSUPPORTED;
+    g->num_blocks = pool->num_blocks;
+    g->block_size = pool->block_size;
+    g->block_shift = log2i(pool->block_size);
+    g->hkv = pool->num_kv_heads;
+    g->d = pool->head_dim;
+    g->dtype = pool->dtype;
+    return PA_OK;
+}
+
+pa_status check_attention_shape(const pa_pool *pool, int32_t num_q_heads, pa::PoolGeom *g) {
+    pa_status st = check_pool(pool, g);
+    if (st != PA_OK) return st;
+    if (num_q_heads <= 0 || num_q_heads % g->hkv) return PA_ERR_BAD_SHAPE;
+    const int group = num_q_heads / g->hkv;
+    if (group != 1 && group != 2 && group != 4 && group != 8) return PA_ERR_UNSUPPORTED;
+    if (g->d != 32 && g->d != 64 && g->d != 128 && g->d != 256) return PA_ERR_UNSUPPORTED;
+    return PA_OK;
+}
+
+pa_status from_hip(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
+
+void say(char *why, size_t why_len, const char *fmt, long long a, long long b) {
+    if (why && why_len) snprintf(why, why_len, fmt, a, b);
+}
+
+}  // namespace
+
+extern "C" {
+
+int pa_abi_version(void) { return PA_ABI_VERSION; }
+
+const char *pa_status_string(pa_status s) {
+    switch (s) {
+        case PA_OK: return "ok";
+        case PA_ERR_NULL_ARG: return "null argument";
+        case PA_ERR_BAD_SHAPE: return "bad shape or size";
+        case PA_ERR_BAD_DTYPE: return "unsupported element type";
+        case PA_ERR_UNSUPPORTED: return "unsupported head_dim, block_size, group size or alignment";
+        case PA_ERR_WORKSPACE: return "workspace missing or too small";
+        case PA_ERR_HIP: return "HIP launch error";
+        case PA_ERR_BAD_METADATA: return "invalid metadata";
+    }
+    return "unknown status";
+}
+
+pa_status pa_store_kv(const void *k, int64_t k_row_stride, const void *v, int64_t v_row_stride,
+                      const int32_t *slot_mapping, int32_t num_tokens, void *k_pool, void *v_pool,
+                      const pa_pool *pool, void *stream) {
+    pa::PoolGeom g;
+    pa_status st = check_pool(pool, &g);
+    if (st != PA_OK) return st;
+    if (num_tokens < 0) return PA_ERR_BAD_SHAPE;
+    if (num_tokens == 0) return PA_OK;
+    if (!k || !v || !slot_mapping || !k_pool || !v_pool) return PA_ERR_NULL_ARG;
+    const int64_t row = (int64_t)g.hkv * g.d;
+    if (k_row_stride < row || v_row_stride < row) return PA_ERR_BAD_SHAPE;
+    return from_hip(pa::launch_store_kv(k, k_row_stride, v, v_row_stride, slot_mapping, num_tokens,
+                                        k_pool, v_pool, g, (hipStream_t)stream));
+}
+
+size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t total_q, int32_t num_q_heads,
+                                  int32_t max_seqlen_q, int32_t max_seqlen_k, const pa_pool *pool) {
+    (void)max_seqlen_q;
+    pa::PoolGeom g;
+    if (check_attention_shape(pool, num_q_heads, &g) != PA_OK) return 0;
+    if (num_seqs <= 0 || total_q <= 0) return 0;
+    const int group = num_q_heads / g.hkv;
+    if (pa::prefill_mfma_supported(g, group)) return 0;
+    const pa::RowAttnPlan plan = pa::plan_row_attention(total_q, g.hkv, g.d, g.dtype, group, max_seqlen_k);
+    return pa::row_attention_workspace_bytes(plan, num_q_heads, g.d);
+}
+
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,
+                                 const pa_pool *pool) {
+    pa::PoolGeom g;
+    if (check_attention_shape(pool, num_q_heads, &g) != PA_OK) return 0;
+    if (num_seqs <= 0 || max_context_len <= 0) return 0;
+    const int group = num_q_heads / g.hkv;
+    const pa::RowAttnPlan plan = pa::plan_row_attention(num_seqs, g.hkv, g.d, g.dtype, group, max_context_len);
+    return pa::row_attention_workspace_bytes(plan, num_q_heads, g.d);
+}
+
+pa_status pa_prefill_varlen(const void *q, int64_t q_row_stride, int32_t num_q_heads,
+                            const void *k_pool, const void *v_pool, const pa_pool *pool,
+                            const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k,
+                            const int32_t *q_offsets, const int32_t *block_table,
+                            int32_t block_table_stride, int32_t num_seqs, int32_t total_q,
+                            int32_t max_seqlen_q, int32_t max_seqlen_k, float softmax_scale,
+                            void *out, void *workspace, size_t workspace_bytes, void *stream) {
+    pa::PoolGeom g;
+    pa_status st = check_attention_shape(pool, num_q_heads, &g);
+    if (st != PA_OK) return st;
+    if (num_seqs < 0 || total_q < 0 || max_seqlen_q < 0 || max_seqlen_k < 0) return PA_ERR_BAD_SHAPE;
+    if (num_seqs == 0 || total_q == 0) return PA_OK;
+    if (!q || !k_pool || !v_pool || !cu_seqlens_q || !cu_seqlens_k || !q_offsets || !block_table || !out)
+        return PA_ERR_NULL_ARG;
+    if (block_table_stride <= 0) return PA_ERR_BAD_SHAPE;
+    if (q_row_stride < (int64_t)num_q_heads * g.d) return PA_ERR_BAD_SHAPE;
+    const int eb = elem_bytes(g.dtype);
+    if (!aligned16(q) || (q_row_stride * eb) % 16 || !aligned16(k_pool) || !aligned16(v_pool))
+        return PA_ERR_UNSUPPORTED;
+    const int group = num_q_heads / g.hkv;
+    if (pa::prefill_mfma_supported(g, group)) {
+        if (!aligned16(out)) return PA_ERR_UNSUPPORTED;
+        return from_hip(pa::launch_prefill_mfma(q, q_row_stride, num_q_heads, k_pool, v_pool, g,
+                                                cu_seqlens_q, cu_seqlens_k, q_offsets, block_table,
+                                                block_table_stride, num_seqs, total_q, max_seqlen_q,
+                                                softmax_scale, out, (hipStream_t)stream));
+    }
+    const pa::RowAttnPlan plan = pa::plan_row_attention(total_q, g.hkv, g.d, g.dtype, group, max_seqlen_k);
+    const size_t need = pa::row_attention_workspace_bytes(plan, num_q_heads, g.d);
+    if (need && (!workspace || workspace_bytes < need)) return PA_ERR_WORKSPACE;
+    return from_hip(pa::launch_prefill_rows(q, q_row_stride, num_q_heads, k_pool, v_pool, g,
+                                            cu_seqlens_q, cu_seqlens_k, q_offsets, block_table,
+                                            block_table_stride, num_seqs, plan, softmax_scale, out,
+                                            workspace, (hipStream_t)stream));
+}
+
+pa_status pa_decode(const void *q, int64_t q_row_stride, int32_t num_q_heads, const void *k_pool,
+                    const void *v_pool, const pa_pool *pool, const int32_t *context_lens,
+                    const int32_t *block_table, int32_t block_table_stride, int32_t num_seqs,
+                    int32_t max_context_len, float softmax_scale, void *out, void *workspace,
+                    size_t workspace_bytes, void *stream) {
+    pa::PoolGeom g;
+    pa_status st = check_attention_shape(pool, num_q_heads, &g);
+    if (st != PA_OK) return st;
+    if (num_seqs < 0 || max_context_len < 0) return PA_ERR_BAD_SHAPE;
+    if (num_seqs == 0) return PA_OK;
+    if (!q || !k_pool || !v_pool || !context_lens || !block_table || !out) return PA_ERR_NULL_ARG;
+    if (block_table_stride <= 0) return PA_ERR_BAD_SHAPE;
+    if (q_row_stride < (int64_t)num_q_heads * g.d) return PA_ERR_BAD_SHAPE;
+    const int eb = elem_bytes(g.dtype);
+    if (!aligned16(q) || (q_row_stride * eb) % 16 || !aligned16(k_pool) || !aligned16(v_pool))
+        return PA_ERR_UNSUPPORTED;
+    const int group = num_q_heads / g.hkv;
+    const pa::RowAttnPlan plan = pa::plan_row_attention(num_seqs, g.hkv, g.d, g.dtype, group, max_context_len);
+    const size_t need = pa::row_attention_workspace_bytes(plan, num_q_heads, g.d);
+    if (need && (!workspace || workspace_bytes < need)) return PA_ERR_WORKSPACE;
+    return from_hip(pa::launch_decode(q, q_row_stride, num_q_heads, k_pool, v_pool, g, context_lens,
+                                      block_table, block_table_stride, plan, softmax_scale, out,
+                                      workspace, (hipStream_t)stream));
+}
+
+pa_status pa_gather_kv(const void *k_pool, const void *v_pool, const pa_pool *pool,
+                       const int32_t *cu_seqlens_k, const int32_t *block_table,
+                       int32_t block_table_stride, int32_t num_seqs, int32_t total_k, void *k_out,
+                       void *v_out, void *stream) {
+    pa::PoolGeom g;
+    pa_status st = check_pool(pool, &g);
+    if (st != PA_OK) return st;
+    if (num_seqs < 0 || total_k < 0) return PA_ERR_BAD_SHAPE;
+    if (num_seqs == 0 || total_k == 0) return PA_OK;
+    if (!k_pool || !v_pool || !cu_seqlens_k || !block_table || !k_out || !v_out) return PA_ERR_NULL_ARG;
+    if (block_table_stride <= 0) return PA_ERR_BAD_SHAPE;
+    if (((int64_t)g.hkv * g.d * elem_bytes(g.dtype)) % 16) return PA_ERR_UNSUPPORTED;
+    if (!aligned16(k_pool) || !aligned16(v_pool) || !aligned16(k_out) || !aligned16(v_out))
+        return PA_ERR_UNSUPPORTED;
+    return from_hip(pa::launch_gather_kv(k_pool, v_pool, g, cu_seqlens_k, block_table,
+                                         block_table_stride, num_seqs, total_k, k_out, v_out,
+                                         (hipStream_t)stream));
+}
+
+static pa_status check_slots(const int32_t *slot_mapping, int32_t num_slots, const pa_pool *pool,
+                             char *why, size_t why_len) {
+    if (!slot_mapping || num_slots <= 0) return PA_OK;
+    const int64_t cap = pool->num_blocks * (int64_t)pool->block_size;
+    std::vector<int32_t> seen;
+    seen.reserve((size_t)num_slots);
+    for (int32_t t = 0; t < num_slots; ++t) {
+        const int32_t s = slot_mapping[t];
+        if (s == -1) continue;
+        if (s < 0 || s >= cap) {
+            say(why, why_len, "slot_mapping[%lld] = %lld out of range", t, s);
+            return PA_ERR_BAD_METADATA;
+        }
+        seen.push_back(s);
+    }
+    std::sort(seen.begin(), seen.end());
+    for (size_t i = 1; i < seen.size(); ++i)
+        if (seen[i] == seen[i - 1]) {
+            say(why, why_len, "slot %lld stored twice (%lld)", seen[i], seen[i]);
+            return PA_ERR_BAD_METADATA;
+        }
+    return PA_OK;
+}
+
+static pa_status check_table_row(const int32_t *block_table, int32_t stride, int32_t s, int64_t keys,
+                                 const pa_pool *pool, char *why, size_t why_len) {
+    const int64_t need = (keys + pool->block_size - 1) / pool->block_size;
+    if (need > stride) {
+        say(why, why_len, "sequence %lld needs %lld blocks, more than the table width", s, need);
+        return PA_ERR_BAD_METADATA;
+    }
+    for (int64_t b = 0; b < need; ++b) {
+        const int32_t p = block_table[(int64_t)s * stride + b];
+        if (p < 0 || p >= pool->num_blocks) {
+            say(why, why_len, "sequence %lld block id %lld out of range", s, p);
+            return PA_ERR_BAD_METADATA;
+        }
+    }
+    return PA_OK;
+}
+
+pa_status pa_validate_prefill_metadata(const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k,
+                                       const int32_t *q_offsets, const int32_t *block_table,
+                                       int32_t block_table_stride, int32_t num_seqs,
+                                       int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                       const int32_t *slot_mapping, int32_t num_slots,
+                                       const pa_pool *pool, char *why, size_t why_len) {
+    if (why && why_len) why[0] = 0;
+    if (!pool) return PA_ERR_NULL_ARG;
+    if (num_seqs < 0) return PA_ERR_BAD_SHAPE;
+    if (num_seqs == 0) return check_slots(slot_mapping, num_slots, pool, why, why_len);
+    if (!cu_seqlens_q || !cu_seqlens_k || !q_offsets || !block_table) return PA_ERR_NULL_ARG;
+    if (pool->block_size <= 0) return PA_ERR_BAD_SHAPE;
+    if (cu_seqlens_q[0] != 0 || cu_seqlens_k[0] != 0) {
+        say(why, why_len, "cu_seqlens must start at 0 (q %lld, k %lld)", cu_seqlens_q[0], cu_seqlens_k[0]);
+        return PA_ERR_BAD_METADATA;
+    }
+    for (int32_t s = 0; s < num_seqs; ++s) {
+        const int64_t ql = (int64_t)cu_seqlens_q[s + 1] - cu_seqlens_q[s];
+        const int64_t kl = (int64_t)cu_seqlens_k[s + 1] - cu_seqlens_k[s];
+        if (ql < 0 || kl < 0) {
+            say(why, why_len, "sequence %lld has a negative length (%lld)", s, ql < 0 ? ql : kl);
+            return PA_ERR_BAD_METADATA;
+        }
+        if (ql > max_seqlen_q || kl > max_seqlen_k) {
+            say(why, why_len, "sequence %lld longer than max_seqlen (%lld)", s, ql > max_seqlen_q ? ql : kl);
+            return PA_ERR_BAD_METADATA;
+        }
+        if ((int64_t)q_offsets[s] + ql != kl) {
+            say(why, why_len, "sequence %lld: q_offset + q_len != k_len (k_len %lld)", s, kl);
+            return PA_ERR_BAD_METADATA;
+        }
+        pa_status st = check_table_row(block_table, block_table_stride, s, kl, pool, why, why_len);
+        if (st != PA_OK) return st;
+    }
+    return check_slots(slot_mapping, num_slots, pool, why, why_len);
+}
+
+pa_status pa_validate_decode_metadata(const int32_t *context_lens, const int32_t *block_table,
+                                      int32_t block_table_stride, int32_t num_seqs,
+                                      int32_t max_context_len, const int32_t *slot_mapping,
+                                      const pa_pool *pool, char *why, size_t why_len) {
+    if (why && why_len) why[0] = 0;
+    if (!pool) return PA_ERR_NULL_ARG;
+    if (num_seqs < 0) return PA_ERR_BAD_SHAPE;
+    if (num_seqs == 0) return PA_OK;
+    if (!context_lens || !block_table) return PA_ERR_NULL_ARG;
+    if (pool->block_size <= 0) return PA_ERR_BAD_SHAPE;
+    for (int32_t s = 0; s < num_seqs; ++s) {
+        if (context_lens[s] < 0 || context_lens[s] > max_context_len) {
+            say(why, why_len, "context_lens[%lld] = %lld outside [0, max_context_len]", s, context_lens[s]);
+            return PA_ERR_BAD_METADATA;
+        }
+        pa_status st = check_table_row(block_table, block_table_stride, s, context_lens[s], pool, why, why_len);
+        if (st != PA_OK) return st;
+    }
+    return check_slots(slot_mapping, num_seqs, pool, why, why_len);
+}
+
+}  // extern "C"

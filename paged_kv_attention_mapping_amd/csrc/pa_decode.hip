@@ -1,0 +1,444 @@
+// pa_decode.hip -- split-K ("flash-decoding") attention of single query rows
+// over the paged KV cache, plus the log-sum-exp merge of the split partials.
+//
+// What it computes (nano-vllm deep dive, Step 4 path C, flash_attn_with_kvcache;
+// Step 5 prepare_decode): for query row r of sequence s with context length
+// ctx, and query head h of KV head g = h / G,
+//     o = sum_j softmax_j(scale * q . k_j) v_j,   j = 0 .. ctx-1,
+// with k_j, v_j found through block_table[s][j / block_size].
+// Split-K (fork Q&A, general Q&A, "what is split-K"): the keys of a row are cut
+// into segments; each segment keeps its own running max m, normaliser l and
+// fp32 accumulator; a second kernel merges the segments by log-sum-exp.
+//
+// Layout on gfx950: one workgroup (4 waves) per (row, KV head g, split).  A
+// token's K row for head g is head_dim contiguous elements; LPT lanes each
+// load 16 bytes of it, so a wave covers 64/LPT tokens per load instruction
+// (bf16, d=128: 16 lanes x 16 B = 256 B per token, 4 tokens per wave).  The G
+// query heads that share KV head g are all served from the same K/V bytes
+// (GQA reuse, fork Q&A Q3 section 2), so every K/V byte is read from HBM once.
+// Scores are reduced across the LPT lanes with DPP row operations.  Phase 1
+// streams K and writes scores (pre-multiplied by scale*log2 e) to LDS;
+// phase 2 takes the split's max; phase 3 streams V, accumulating
+// exp2(s - m) * v.  Block ids of a split are staged in LDS once.
+//
+// The same kernel also serves as the vector-ALU prefill path: a prefill row is
+// one packed query token whose context is min(q_offset + i + 1, k_len) keys.
+#include <math.h>
+
+#include "pa_device.h"
+#include "pa_kernels.h"
+
+namespace pa {
+namespace {
+
+constexpr int kNW = 4;        // waves per workgroup
+constexpr int kThreads = kNW * kWave;
+constexpr int kUnroll = 8;    // 16-byte loads in flight per lane per phase
+constexpr int kSplitMax = 1024;  // keys per split, upper bound
+constexpr float kLog2e = 1.4426950408889634f;
+
+template <typename T, int D>
+struct RowCfg {
+    static constexpr int EPV = 16 / Elem<T>::bytes;  // elements per 16-byte vector
+    static constexpr int LPT = D / EPV;              // lanes per token row
+    static constexpr int TPW = kWave / LPT;          // tokens per wave per load
+    static constexpr int TPR = kNW * TPW * kUnroll;  // tokens per round
+    static_assert(LPT >= 1 && LPT <= kWave && kWave % LPT == 0, "head_dim");
+    static_assert(kSplitMax % TPR == 0, "split");
+};
+
+struct DecodeRows {
+    const int32_t *context_lens;
+    __device__ __forceinline__ void get(int r, int &seq, int &ctx) const {
+        seq = r;
+        ctx = context_lens[r];
+    }
+};
+
+struct PrefillRows {
+    const int32_t *cu_q;
+    const int32_t *cu_k;
+    const int32_t *q_off;
+    int num_seqs;
+    __device__ __forceinline__ void get(int r, int &seq, int &ctx) const {
+        int lo = 0, hi = num_seqs;  // cu_q[lo] <= r < cu_q[hi]
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (cu_q[mid] <= r) lo = mid; else hi = mid;
+        }
+        seq = lo;
+        const int i = r - cu_q[lo];
+        const int k_len = cu_k[lo + 1] - cu_k[lo];
+        ctx = min(q_off[lo] + i + 1, k_len);
+    }
+};
+
+struct RowArgs {
+    const void *q;
+    int64_t q_row_stride;      // elements
+    const void *k_pool;
+    const void *v_pool;
+    int64_t num_blocks;
+    int block_shift;
+    int hkv;
+    const int32_t *block_table;
+    int bt_stride;
+    int num_rows;
+    int num_splits;
+    int split_tokens;
+    float scale_log2;          // softmax_scale * log2(e)
+    void *out;
+    float *ws_acc;             // [rows][hq][splits][D]
+    float *ws_m;               // [rows][hq][splits]
+    float *ws_l;
+};
+
+template <typename T, int D, int G, class Rows>
+__global__ __launch_bounds__(kThreads) void row_attn_split(RowArgs a, Rows rows) {
+    using C = RowCfg<T, D>;
+    constexpr int EPV = C::EPV, LPT = C::LPT, TPW = C::TPW, TPR = C::TPR;
+    static_assert(kNW * D <= kSplitMax, "accumulator staging aliases the score buffer");
+    __shared__ float s_buf[G * kSplitMax];   // scores [G][split], later [kNW][G][D]
+    __shared__ int s_blk[kSplitMax];         // physical block ids of this split
+    __shared__ float s_l[kNW][G];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1), w = tid >> 6;
+    const int tg = lane / LPT, c = lane % LPT;
+    const int hkv = a.hkv, hq = hkv * G;
+
+    const int64_t wg = blockIdx.x;
+    const int g = (int)(wg % hkv);
+    const int64_t rest = wg / hkv;
+    const int split = (int)(rest % a.num_splits);
+    const int row = (int)(rest / a.num_splits);
+    int seq, ctx;
+    rows.get(row, seq, ctx);
+    // Never index past the table row or past the splits the launch covers.
+    ctx = (int)min((int64_t)ctx, min((int64_t)a.bt_stride << a.block_shift,
+                                     (int64_t)a.num_splits * a.split_tokens));
+
+    T *out_row = reinterpret_cast<T *>(a.out) + ((int64_t)row * hq + (int64_t)g * G) * D;
+    const int t0 = split * a.split_tokens;
+    if (t0 >= ctx) {
+        if (split == 0)  // no visible key: defined as a zero output
+            for (int i = tid; i < G * D; i += kThreads) store_elem<T>(out_row + i, 0.f);
+        return;
+    }
+    const int t1 = min(t0 + a.split_tokens, ctx);
+    const int n = t1 - t0;
+    const int nsplit_row = (ctx + a.split_tokens - 1) / a.split_tokens;
+    const int shift = a.block_shift;
+    const int bmask = (1 << shift) - 1;
+    const int b0 = t0 >> shift;
+
+    {   // stage the block ids this split needs; ids outside the pool are masked
+        const int32_t *bt = a.block_table + (int64_t)seq * a.bt_stride;
+        const int nb = ((t1 - 1) >> shift) - b0 + 1;
+        for (int i = tid; i < nb; i += kThreads) {
+            const int p = bt[b0 + i];
+            s_blk[i] = (p >= 0 && (int64_t)p < a.num_blocks) ? p : -1;
+        }
+    }
+
+    // this lane's slice of the G query heads, pre-scaled by scale*log2(e)
+    float qv[G][EPV];
+    {
+        const T *qrow = reinterpret_cast<const T *>(a.q) + (int64_t)row * a.q_row_stride + (int64_t)g * G * D;
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            unpack16<T>(ld16(qrow + j * D + c * EPV), qv[j]);
+#pragma unroll
+            for (int e = 0; e < EPV; ++e) qv[j][e] *= a.scale_log2;
+        }
+    }
+    __syncthreads();
+
+    const T *kp = reinterpret_cast<const T *>(a.k_pool);
+    const T *vp = reinterpret_cast<const T *>(a.v_pool);
+    const int64_t head_off = (int64_t)g * D + c * EPV;
+
+    // ---- phase 1: scores -------------------------------------------------
+    for (int base = t0; base < t1; base += TPR) {
+        uint4 kr[kUnroll];
+        unsigned valid = 0;
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int tok = base + (u * kNW + w) * TPW + tg;
+            int p = -1;
+            if (tok < t1) p = s_blk[(tok >> shift) - b0];
+            if (p >= 0) {
+                const int64_t slot = ((int64_t)p << shift) + (tok & bmask);
+                kr[u] = ld16(kp + slot * hkv * D + head_off);
+                valid |= 1u << u;
+            } else {
+                kr[u] = make_uint4(0, 0, 0, 0);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int tok = base + (u * kNW + w) * TPW + tg;
+            float kf[EPV];
+            unpack16<T>(kr[u], kf);
+#pragma unroll
+            for (int j = 0; j < G; ++j) {
+                float dot = 0.f;
+#pragma unroll
+                for (int e = 0; e < EPV; ++e) dot = fmaf(qv[j][e], kf[e], dot);
+                dot = group_sum<LPT>(dot);
+                if (c == 0 && tok < t1) s_buf[j * kSplitMax + (tok - t0)] = ((valid >> u) & 1) ? dot : -INFINITY;
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- phase 2: split max per head (every wave computes the same value) --
+    float m[G];
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+        float x = -INFINITY;
+        for (int i = lane; i < n; i += kWave) x = fmaxf(x, s_buf[j * kSplitMax + i]);
+        x = group_max<kWave>(x);
+        m[j] = (x == -INFINITY) ? 0.f : x;
+    }
+
+    // ---- phase 3: exp2(s - m) * v ------------------------------------------
+    float acc[G][EPV];
+    float l[G];
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+        l[j] = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) acc[j][e] = 0.f;
+    }
+    for (int base = t0; base < t1; base += TPR) {
+        uint4 vr[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int tok = base + (u * kNW + w) * TPW + tg;
+            int p = -1;
+            if (tok < t1) p = s_blk[(tok >> shift) - b0];
+            if (p >= 0) {
+                const int64_t slot = ((int64_t)p << shift) + (tok & bmask);
+                vr[u] = ld16(vp + slot * hkv * D + head_off);
+            } else {
+                vr[u] = make_uint4(0, 0, 0, 0);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int tok = base + (u * kNW + w) * TPW + tg;
+            if (tok < t1) {
+                float vf[EPV];
+                unpack16<T>(vr[u], vf);
+#pragma unroll
+                for (int j = 0; j < G; ++j) {
+                    const float pj = exp2f(s_buf[j * kSplitMax + (tok - t0)] - m[j]);
+                    l[j] += pj;
+#pragma unroll
+                    for (int e = 0; e < EPV; ++e) acc[j][e] = fmaf(pj, vf[e], acc[j][e]);
+                }
+            }
+        }
+    }
+
+    // ---- reduce over the token groups of a wave, then over waves ----------
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+        l[j] = cross_group_sum<LPT>(l[j]);
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) acc[j][e] = cross_group_sum<LPT>(acc[j][e]);
+    }
+    __syncthreads();  // every wave is done reading scores; reuse s_buf
+    float *s_acc = s_buf;  // [kNW][G][D]
+    if (tg == 0) {
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+#pragma unroll
+            for (int e = 0; e < EPV; ++e) s_acc[(w * G + j) * D + c * EPV + e] = acc[j][e];
+            if (c == 0) s_l[w][j] = l[j];
+        }
+    }
+    __syncthreads();
+    for (int i = tid; i < G * D; i += kThreads) {
+        const int j = i / D, d = i - j * D;
+        float A = 0.f, L = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < kNW; ++ww) {
+            A += s_acc[(ww * G + j) * D + d];
+            L += s_l[ww][j];
+        }
+        if (nsplit_row == 1) {
+            store_elem<T>(out_row + i, L > 0.f ? A / L : 0.f);
+        } else {
+            const int64_t idx = ((int64_t)row * hq + g * G + j) * a.num_splits + split;
+            a.ws_acc[idx * D + d] = A;
+            if (d == 0) {
+                a.ws_m[idx] = m[j];
+                a.ws_l[idx] = L;
+            }
+        }
+    }
+}
+
+struct MergeArgs {
+    int num_rows;
+    int hq;
+    int num_splits;
+    int split_tokens;
+    int bt_stride;
+    int block_shift;
+    const float *ws_acc;
+    const float *ws_m;
+    const float *ws_l;
+    void *out;
+};
+
+// One wave per (row, query head): out = sum_c acc_c 2^(m_c - m*) / sum_c l_c 2^(m_c - m*).
+template <typename T, int D, class Rows>
+__global__ __launch_bounds__(kThreads) void row_attn_merge(MergeArgs a, Rows rows) {
+    const int64_t wave = (int64_t)blockIdx.x * kNW + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & (kWave - 1);
+    if (wave >= (int64_t)a.num_rows * a.hq) return;
+    const int row = (int)(wave / a.hq), h = (int)(wave % a.hq);
+    int seq, ctx;
+    rows.get(row, seq, ctx);
+    ctx = (int)min((int64_t)ctx, min((int64_t)a.bt_stride << a.block_shift,
+                                     (int64_t)a.num_splits * a.split_tokens));
+    const int ns = (ctx + a.split_tokens - 1) / a.split_tokens;
+    if (ns <= 1) return;  // written directly by the split kernel
+    const int64_t base = ((int64_t)row * a.hq + h) * a.num_splits;
+    float mstar = -INFINITY;
+    for (int s = 0; s < ns; ++s) mstar = fmaxf(mstar, a.ws_m[base + s]);
+    float L = 0.f;
+    for (int s = 0; s < ns; ++s) L += a.ws_l[base + s] * exp2f(a.ws_m[base + s] - mstar);
+    T *o = reinterpret_cast<T *>(a.out) + ((int64_t)row * a.hq + h) * D;
+    for (int d = lane; d < D; d += kWave) {
+        float A = 0.f;
+        for (int s = 0; s < ns; ++s) A += a.ws_acc[(base + s) * D + d] * exp2f(a.ws_m[base + s] - mstar);
+        store_elem<T>(o + d, L > 0.f ? A / L : 0.f);
+    }
+}
+
+int tokens_per_round(int dtype, int d) {
+    const int epv = dtype == 0 ? 4 : 8;
+    const int lpt = d / epv;
+    return kNW * (kWave / lpt) * kUnroll;
+}
+
+template <typename T, int D, int G, class Rows>
+hipError_t run_rows(const RowArgs &a, const Rows &rows, hipStream_t stream) {
+    const int64_t wgs = (int64_t)a.num_rows * a.num_splits * a.hkv;
+    if (wgs == 0) return hipSuccess;
+    hipLaunchKernelGGL((row_attn_split<T, D, G, Rows>), dim3((unsigned)wgs), dim3(kThreads), 0, stream,
+                       a, rows);
+    if (a.num_splits > 1) {
+        MergeArgs m{a.num_rows, a.hkv * G, a.num_splits, a.split_tokens, a.bt_stride, a.block_shift,
+                    a.ws_acc, a.ws_m, a.ws_l, a.out};
+        const int64_t waves = (int64_t)a.num_rows * a.hkv * G;
+        hipLaunchKernelGGL((row_attn_merge<T, D, Rows>), dim3((unsigned)((waves + kNW - 1) / kNW)),
+                           dim3(kThreads), 0, stream, m, rows);
+    }
+    return hipGetLastError();
+}
+
+template <typename T, int D, class Rows>
+hipError_t dispatch_group(int group, const RowArgs &a, const Rows &rows, hipStream_t s) {
+    switch (group) {
+        case 1: return run_rows<T, D, 1>(a, rows, s);
+        case 2: return run_rows<T, D, 2>(a, rows, s);
+        case 4: return run_rows<T, D, 4>(a, rows, s);
+        case 8: return run_rows<T, D, 8>(a, rows, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <typename T, class Rows>
+hipError_t dispatch_dim(int d, int group, const RowArgs &a, const Rows &rows, hipStream_t s) {
+    switch (d) {
+        case 32: return dispatch_group<T, 32>(group, a, rows, s);
+        case 64: return dispatch_group<T, 64>(group, a, rows, s);
+        case 128: return dispatch_group<T, 128>(group, a, rows, s);
+        case 256: return dispatch_group<T, 256>(group, a, rows, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <class Rows>
+hipError_t dispatch(const PoolGeom &g, int group, const RowArgs &a, const Rows &rows, hipStream_t s) {
+    return g.dtype == 0 ? dispatch_dim<float>(g.d, group, a, rows, s)
+                        : dispatch_dim<bf16_t>(g.d, group, a, rows, s);
+}
+
+RowArgs make_args(const void *q, int64_t q_row_stride, int hq, const void *k_pool, const void *v_pool,
+                  const PoolGeom &g, const int32_t *block_table, int bt_stride,
+                  const RowAttnPlan &plan, float softmax_scale, void *out, void *workspace) {
+    RowArgs a{};
+    a.q = q;
+    a.q_row_stride = q_row_stride;
+    a.k_pool = k_pool;
+    a.v_pool = v_pool;
+    a.num_blocks = g.num_blocks;
+    a.block_shift = g.block_shift;
+    a.hkv = g.hkv;
+    a.block_table = block_table;
+    a.bt_stride = bt_stride;
+    a.num_rows = plan.num_rows;
+    a.num_splits = plan.num_splits;
+    a.split_tokens = plan.split_tokens;
+    a.scale_log2 = softmax_scale * kLog2e;
+    a.out = out;
+    if (plan.num_splits > 1) {
+        const int64_t n = (int64_t)plan.num_rows * hq * plan.num_splits;
+        float *ws = reinterpret_cast<float *>(workspace);
+        a.ws_acc = ws;
+        a.ws_m = ws + n * g.d;
+        a.ws_l = a.ws_m + n;
+    }
+    return a;
+}
+
+}  // namespace
+
+RowAttnPlan plan_row_attention(int num_rows, int hkv, int d, int dtype, int group, int max_keys) {
+    (void)group;
+    RowAttnPlan p{num_rows, 1, kSplitMax};
+    if (num_rows <= 0 || max_keys <= 0) return p;
+    const int tpr = tokens_per_round(dtype, d);
+    const int64_t target_wgs = 2048;  // ~8 workgroups per CU on 256 CUs
+    int split = kSplitMax;
+    auto wgs = [&](int s) { return (int64_t)num_rows * hkv * ((max_keys + s - 1) / s); };
+    while (split > tpr && wgs(split) < target_wgs) split >>= 1;
+    p.split_tokens = split;
+    p.num_splits = (max_keys + split - 1) / split;
+    return p;
+}
+
+size_t row_attention_workspace_bytes(const RowAttnPlan &p, int hq, int d) {
+    if (p.num_splits <= 1) return 0;
+    const size_t n = (size_t)p.num_rows * hq * p.num_splits;
+    return n * (size_t)(d + 2) * sizeof(float);
+}
+
+hipError_t launch_decode(const void *q, int64_t q_row_stride, int hq, const void *k_pool,
+                         const void *v_pool, const PoolGeom &g, const int32_t *context_lens,
+                         const int32_t *block_table, int bt_stride, const RowAttnPlan &plan,
+                         float softmax_scale, void *out, void *workspace, hipStream_t stream) {
+    const RowArgs a = make_args(q, q_row_stride, hq, k_pool, v_pool, g, block_table, bt_stride, plan,
+                                softmax_scale, out, workspace);
+    return dispatch(g, hq / g.hkv, a, DecodeRows{context_lens}, stream);
+}
+
+hipError_t launch_prefill_rows(const void *q, int64_t q_row_stride, int hq, const void *k_pool,
+                               const void *v_pool, const PoolGeom &g, const int32_t *cu_seqlens_q,
+                               const int32_t *cu_seqlens_k, const int32_t *q_offsets,
+                               const int32_t *block_table, int bt_stride, int num_seqs,
+                               const RowAttnPlan &plan, float softmax_scale, void *out,
+                               void *workspace, hipStream_t stream) {
+    const RowArgs a = make_args(q, q_row_stride, hq, k_pool, v_pool, g, block_table, bt_stride, plan,
+                                softmax_scale, out, workspace);
+    return dispatch(g, hq / g.hkv, a, PrefillRows{cu_seqlens_q, cu_seqlens_k, q_offsets, num_seqs},
+                    stream);
+}
+
+}  // namespace pa

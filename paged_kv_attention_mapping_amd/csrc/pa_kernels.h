@@ -1,0 +1,65 @@
+// pa_kernels.h -- internal launchers of libpa (host side).  Not part of the
+// C ABI; the extern "C" entry points in pa_api.cpp validate arguments and
+// call these.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pa {
+
+// Geometry of one layer's K (and V) pool: [num_blocks][block_size][hkv][d].
+struct PoolGeom {
+    int64_t num_blocks;
+    int block_size;    // power of two
+    int block_shift;   // log2(block_size)
+    int hkv;
+    int d;
+    int dtype;         // 0 fp32, 1 bf16
+};
+
+// Store / gather ---------------------------------------------------------
+hipError_t launch_store_kv(const void *k, int64_t k_row_stride, const void *v, int64_t v_row_stride,
+                           const int32_t *slot_mapping, int num_tokens, void *k_pool, void *v_pool,
+                           const PoolGeom &g, hipStream_t stream);
+
+hipError_t launch_gather_kv(const void *k_pool, const void *v_pool, const PoolGeom &g,
+                            const int32_t *cu_seqlens_k, const int32_t *block_table, int bt_stride,
+                            int num_seqs, int total_k, void *k_out, void *v_out, hipStream_t stream);
+
+// Split-K row attention (decode, and the vector-ALU prefill path) ---------
+// A "row" is one query token: row r of a decode batch is sequence r; row r
+// of a prefill batch is packed query token r.
+struct RowAttnPlan {
+    int num_rows;
+    int num_splits;     // splits per row (grid dimension)
+    int split_tokens;   // keys per split
+};
+
+// Splits are chosen from host sizes only, so workspace size and launch agree.
+RowAttnPlan plan_row_attention(int num_rows, int hkv, int d, int dtype, int group,
+                               int max_keys);
+size_t row_attention_workspace_bytes(const RowAttnPlan &p, int hq, int d);
+
+hipError_t launch_decode(const void *q, int64_t q_row_stride, int hq, const void *k_pool,
+                         const void *v_pool, const PoolGeom &g, const int32_t *context_lens,
+                         const int32_t *block_table, int bt_stride, const RowAttnPlan &plan,
+                         float softmax_scale, void *out, void *workspace, hipStream_t stream);
+
+hipError_t launch_prefill_rows(const void *q, int64_t q_row_stride, int hq, const void *k_pool,
+                               const void *v_pool, const PoolGeom &g, const int32_t *cu_seqlens_q,
+                               const int32_t *cu_seqlens_k, const int32_t *q_offsets,
+                               const int32_t *block_table, int bt_stride, int num_seqs,
+                               const RowAttnPlan &plan, float softmax_scale, void *out,
+                               void *workspace, hipStream_t stream);
+
+// MFMA prefill (bf16, head_dim 64 / 128) ----------------------------------
+bool prefill_mfma_supported(const PoolGeom &g, int group);
+hipError_t launch_prefill_mfma(const void *q, int64_t q_row_stride, int hq, const void *k_pool,
+                               const void *v_pool, const PoolGeom &g, const int32_t *cu_seqlens_q,
+                               const int32_t *cu_seqlens_k, const int32_t *q_offsets,
+                               const int32_t *block_table, int bt_stride, int num_seqs, int total_q,
+                               int max_seqlen_q, float softmax_scale, void *out, hipStream_t stream);
+
+}  // namespace pa

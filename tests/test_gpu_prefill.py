@@ -1,0 +1,143 @@
+"""pa_prefill_varlen on the GPU against the fp64 oracle, element by element
+(max-abs 2e-2 for bf16, 1e-5 for fp32), on the configurations and edge cases."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_attention_mapping_amd as pa
+import workloads as W
+from helpers import host_pools_with_prefix, max_abs_err, say, to_dev, to_host_bits, tol
+
+pytestmark = pytest.mark.gpu
+
+
+def run_prefill(case, rows=None):
+    """Store the new tokens on the GPU, prefill, and return (gpu_out, oracle_out, host pools)."""
+    kp, vp = host_pools_with_prefix(case)
+    kd, vd = to_dev(kp), to_dev(vp)
+    pa.pa_store_kv(to_dev(case.k_new), to_dev(case.v_new), to_dev(case.slot_new), kd, vd)
+    oracle.store_kv(case.k_new, case.v_new, case.slot_new, kp, vp)
+    out = pa.pa_prefill_varlen(to_dev(case.q), kd, vd, to_dev(case.cu_seqlens_q), to_dev(case.cu_seqlens_k),
+                               to_dev(np.asarray(case.q_offsets, np.int32)), to_dev(case.block_table),
+                               case.max_seqlen_q, case.max_seqlen_k, case.scale)
+    torch.cuda.synchronize()
+    ref = oracle.prefill(case.q, kp, vp, case.cu_seqlens_q, case.cu_seqlens_k, case.q_offsets,
+                         case.block_table, case.scale, rows=rows)
+    got = out if rows is None else out[torch.as_tensor(np.asarray(rows), device=out.device).long()]
+    return got, ref, (kp, vp, kd, vd, out)
+
+
+def sample_rows(case, n, seed):
+    """Seeded sample of packed rows, always including every sequence's first
+    and last row and the heaviest (last) rows of the batch."""
+    rng = np.random.default_rng(seed)
+    cu = case.cu_seqlens_q
+    must = set()
+    for s in range(case.num_seqs):
+        if cu[s + 1] > cu[s]:
+            must.update([int(cu[s]), int(cu[s + 1]) - 1])
+    must.update(range(max(0, case.total_q - 8), case.total_q))
+    extra = rng.choice(case.total_q, size=min(n, case.total_q), replace=False)
+    return np.array(sorted(must | set(extra.tolist())), dtype=np.int32)
+
+
+def test_c1_tiny_fp32():
+    pre, _ = W.c1_tiny()
+    say("[prefill] c1 fp32")
+    got, ref, _ = run_prefill(pre)
+    assert max_abs_err(got, ref) <= tol("f32")
+
+
+@pytest.mark.parametrize("n", [32, 128, 256])
+def test_c2_varlen_bf16(n):
+    case = W.c2_varlen(n)
+    say(f"[prefill] c2 8x{n}")
+    got, ref, _ = run_prefill(case)
+    err = max_abs_err(got, ref)
+    say(f"  max-abs {err:.3e}")
+    assert err <= tol("bf16")
+
+
+def test_c3_prefix_suffix_and_full_rows():
+    """C3: the 44-token suffix over a cached 256-token block; also equal (within
+    tolerance) to rows 256..299 of a full 300-token prefill on the GPU."""
+    case = W.c3_prefix()
+    say("[prefill] c3 prefix")
+    got, ref, (kp, vp, kd, vd, out) = run_prefill(case)
+    assert max_abs_err(got, ref) <= tol("bf16")
+    # full prefill of the same 300 tokens (queries of the cached part drawn fresh)
+    rng = np.random.default_rng(1)
+    q_full = W.normal(rng, (600, 16, 128), "bf16")
+    q_full[256:300] = case.q[:44]
+    q_full[556:600] = case.q[44:]
+    full = pa.pa_prefill_varlen(to_dev(q_full), kd, vd, to_dev(np.array([0, 300, 600], np.int32)),
+                                to_dev(case.cu_seqlens_k), to_dev(np.zeros(2, np.int32)),
+                                to_dev(case.block_table), 300, 300, case.scale)
+    torch.cuda.synchronize()
+    rows = np.r_[256:300, 556:600]
+    assert max_abs_err(full[torch.as_tensor(rows, device="cuda")], ref) <= tol("bf16")
+
+
+def test_c5a_long_4096_sampled_rows():
+    case = W.c5a_long()
+    rows = sample_rows(case, 48, 5096)
+    say(f"[prefill] c5a 1x4096, {len(rows)} sampled rows")
+    got, ref, _ = run_prefill(case, rows=rows)
+    err = max_abs_err(got, ref)
+    say(f"  max-abs {err:.3e}")
+    assert err <= tol("bf16")
+
+
+def test_c5a_mixed_chunked_sampled_rows():
+    case = W.c5a_mixed()
+    rows = sample_rows(case, 160, 5192)
+    say(f"[prefill] c5a mixed {case.num_seqs} seqs, {len(rows)} sampled rows")
+    got, ref, _ = run_prefill(case, rows=rows)
+    assert max_abs_err(got, ref) <= tol("bf16")
+
+
+@pytest.mark.parametrize("dtype,d,hq,hkv,bs", [
+    ("bf16", 128, 16, 8, 16), ("bf16", 64, 8, 1, 32), ("bf16", 128, 4, 4, 1), ("bf16", 32, 4, 2, 16),
+    ("bf16", 256, 4, 2, 16), ("f32", 128, 8, 2, 16), ("f32", 64, 8, 8, 4), ("bf16", 128, 32, 4, 64),
+])
+def test_ragged_shapes_and_offsets(dtype, d, hq, hkv, bs):
+    """Ragged lengths spanning several tiles plus tails, arbitrary cached
+    prefixes (not block aligned), a zero-length sequence in the middle."""
+    q_lens = [1, 67, 0, 130, 5, 200]
+    q_offs = [0, 13, 9, 0, 250, 61]
+    case = W.make_prefill("ragged", 100 + d + hq, q_lens, q_offs, hq, hkv, d, bs, dtype)
+    say(f"[prefill] ragged {dtype} d={d} {hq}/{hkv} bs={bs}")
+    got, ref, _ = run_prefill(case)
+    assert max_abs_err(got, ref) <= tol(dtype)
+
+
+def test_single_visible_key_rows_return_v():
+    """Row 0 of a fresh prompt sees key 0 only: the output is V[0] (to bf16 rounding)."""
+    case = W.make_prefill("one", 8, [1, 64, 129], [0, 0, 0], 16, 8, 128, 16, "bf16")
+    say("[prefill] single-key rows")
+    got, ref, _ = run_prefill(case)
+    for s in range(3):
+        r = int(case.cu_seqlens_q[s])
+        g = to_host_bits(got[r])
+        v = np.repeat(case.v_new[r], 2, axis=0)
+        assert (g == v).all()
+
+
+def test_block_permutation_invariance_and_determinism():
+    case = W.make_prefill("perm", 9, [300, 77], [20, 0], 16, 8, 128, 16, "bf16")
+    say("[prefill] permutation + determinism")
+    got, ref, (kp, vp, kd, vd, out) = run_prefill(case)
+    q = to_dev(case.q)
+    args = (to_dev(case.cu_seqlens_q), to_dev(case.cu_seqlens_k), to_dev(np.asarray(case.q_offsets, np.int32)))
+    again = pa.pa_prefill_varlen(q, kd, vd, *args, to_dev(case.block_table), case.max_seqlen_q,
+                                 case.max_seqlen_k, case.scale)
+    perm = np.random.default_rng(2).permutation(case.num_blocks)
+    kp2, vp2 = np.empty_like(kp), np.empty_like(vp)
+    kp2[perm], vp2[perm] = kp, vp
+    perm_out = pa.pa_prefill_varlen(q, to_dev(kp2), to_dev(vp2), *args,
+                                    to_dev(perm[case.block_table].astype(np.int32)), case.max_seqlen_q,
+                                    case.max_seqlen_k, case.scale)
+    torch.cuda.synchronize()
+    assert to_host_bits(again).tobytes() == to_host_bits(out).tobytes()
+    assert max_abs_err(perm_out, ref) <= tol("bf16")
