@@ -1,0 +1,242 @@
+"""Throughput of the paged-KV attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+One step = one pass of the whole path at Qwen3-0.6B attention shapes (16 q /
+8 kv heads, head_dim 128, bf16):
+  * prefill  : pa_store_kv of a 4096-token prompt, then pa_prefill_varlen
+               (1 sequence x 4096, causal, block_size 16);
+  * decode   : for each of 28 layers, pa_store_kv of the 256 new tokens, then
+               pa_decode over 256 sequences with contexts uniform in
+               [100, 2048] (block_size 256, one KV pool per layer).
+Inputs are synthetic (seeded) and resident in HBM before timing starts.
+
+Prints ONE JSON line.  `value` is the decode KV read rate (GB/s: bytes of
+every visible K and V row, once per KV head, over the decode calls' time);
+`prefill.value` is the prefill rate (TFLOP/s: 4*d*Hq per visible causal
+pair over the prefill call's time).  Both come from HIP events recorded on
+the stream the kernels run on.  `roofline` is for the decode kernel (the
+dominant cost), `prefill.roofline` for the prefill kernel.  `cpu_baseline`
+times the fp64 CPU oracle on a bounded sample of the same decode workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--layers", type=int, default=28)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="also run one plain 1 GiB device copy (HBM counter calibration)")
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build measures one GPU only (the kernels run on one GPU's share); "
+              "run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import paged_kv_attention_mapping_amd as pa
+    import workloads as W
+
+    torch.cuda.set_device(0)
+    dev = "cuda"
+
+    def to_dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    # ---------------- prefill input: 1 x 4096, block 16 ----------------------
+    pf = W.c5a_long()
+    pf_k, pf_v = (torch.zeros((pf.num_blocks, pf.block_size, pf.num_kv_heads, pf.head_dim),
+                              dtype=torch.bfloat16, device=dev) for _ in range(2))
+    pf_q, pf_kn, pf_vn = to_dev(pf.q), to_dev(pf.k_new), to_dev(pf.v_new)
+    pf_slots = to_dev(pf.slot_new)
+    pf_cuq, pf_cuk = to_dev(pf.cu_seqlens_q), to_dev(pf.cu_seqlens_k)
+    pf_off, pf_bt = to_dev(np.asarray(pf.q_offsets, np.int32)), to_dev(pf.block_table)
+    pf_out = torch.empty_like(pf_q)
+    pf_ws_bytes = pa.pa_prefill_workspace_bytes(1, pf.total_q, pf.num_q_heads, pf.max_seqlen_q,
+                                                pf.max_seqlen_k, pf_k)
+    pf_ws = torch.empty(max(pf_ws_bytes, 1), dtype=torch.uint8, device=dev)
+    pf_flops = 4.0 * pf.head_dim * pf.num_q_heads * pf.causal_pairs
+
+    # ---------------- decode input: 256 x U[100,2048], 28 layer pools -------
+    lay = W.c4_decode_layout()
+    L = args.layers
+    nb, bs, hkv, d, hq = lay.num_blocks, lay.block_size, lay.num_kv_heads, lay.head_dim, lay.num_q_heads
+    k_pools, v_pools, qs, k_news, v_news = [], [], [], [], []
+    for layer in range(L):
+        k_pools.append(W.device_normal((nb, bs, hkv, d), 4100 + 2 * layer))
+        v_pools.append(W.device_normal((nb, bs, hkv, d), 4101 + 2 * layer))
+        qs.append(W.device_normal((lay.num_seqs, hq, d), 9000 + layer))
+        k_news.append(W.device_normal((lay.num_seqs, hkv, d), 7000 + 2 * layer))
+        v_news.append(W.device_normal((lay.num_seqs, hkv, d), 7001 + 2 * layer))
+    ctx_d, bt_d, slot_d = to_dev(lay.context_lens), to_dev(lay.block_table), to_dev(lay.slot_new)
+    dec_out = torch.empty((lay.num_seqs, hq, d), dtype=torch.bfloat16, device=dev)
+    ws_bytes = pa.pa_decode_workspace_bytes(lay.num_seqs, hq, lay.max_context_len, k_pools[0])
+    dec_ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    kv_bytes_layer = lay.kv_bytes()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        # prefill: store the prompt's K/V, then causal varlen attention
+        if ev is not None:
+            ev["pf"][0].record(stream)
+        pa.pa_store_kv(pf_kn, pf_vn, pf_slots, pf_k, pf_v)
+        if ev is not None:
+            ev["pf_attn"][0].record(stream)
+        pa.pa_prefill_varlen(pf_q, pf_k, pf_v, pf_cuq, pf_cuk, pf_off, pf_bt, pf.max_seqlen_q,
+                             pf.max_seqlen_k, pf.scale, out=pf_out, workspace=pf_ws)
+        if ev is not None:
+            ev["pf_attn"][1].record(stream)
+            ev["pf"][1].record(stream)
+        # decode: every layer stores its new token then attends
+        for layer in range(L):
+            pa.pa_store_kv(k_news[layer], v_news[layer], slot_d, k_pools[layer], v_pools[layer])
+            if ev is not None:
+                ev["dec"][layer][0].record(stream)
+            pa.pa_decode(qs[layer], k_pools[layer], v_pools[layer], ctx_d, bt_d, lay.max_context_len,
+                         lay.scale, out=dec_out, workspace=dec_ws)
+            if ev is not None:
+                ev["dec"][layer][1].record(stream)
+
+    def new_events():
+        mk = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+        return {"pf": (mk(), mk()), "pf_attn": (mk(), mk()), "dec": [(mk(), mk()) for _ in range(L)]}
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    per_step_events = [new_events() for _ in range(args.steps)]
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(per_step_events[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+
+    ms_total = t_start.elapsed_time(t_end)
+    ms_per_step = ms_total / args.steps
+    dec_ms = [e["dec"][l][0].elapsed_time(e["dec"][l][1]) for e in per_step_events for l in range(L)]
+    pf_attn_ms = [e["pf_attn"][0].elapsed_time(e["pf_attn"][1]) for e in per_step_events]
+    pf_ms = [e["pf"][0].elapsed_time(e["pf"][1]) for e in per_step_events]
+    dec_call_ms = float(np.mean(dec_ms))
+    decode_gbps = kv_bytes_layer * L * args.steps / (sum(dec_ms) * 1e-3) / 1e9
+    pf_call_ms = float(np.mean(pf_attn_ms))
+    prefill_tflops = pf_flops / (pf_call_ms * 1e-3) / 1e12
+
+    if args.calibrate_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(lay, k_pools[0], v_pools[0], qs[0])
+
+    result = {
+        "metric": "paged-attn decode KV GB/s + prefill TFLOP/s (Qwen3-0.6B shapes, 1 GPU)",
+        "value": round(decode_gbps, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) K/V/Q; seeded lengths and shuffled block tables)",
+        "config": {
+            "workload": (f"qwen3-0.6b attention step: store+prefill 1x4096 causal (block 16) + "
+                         f"{L} layers x (store 256 + decode 256 seqs, ctx U[100,2048], block 256)"),
+            "num_q_heads": hq, "num_kv_heads": hkv, "head_dim": d,
+            "decode_seqs": lay.num_seqs, "decode_sum_ctx": int(lay.context_lens.sum()),
+            "decode_layers": L, "prefill_tokens": pf.total_q,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "pa_decode (split-K kernel + log-sum-exp merge), one call per layer",
+            "achieved": round(kv_bytes_layer / (dec_call_ms * 1e-3) / 1e9, 2),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(kv_bytes_layer / (dec_call_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "traffic": None,
+            "bytes_per_launch": kv_bytes_layer,
+            "avg_launch_us": round(dec_call_ms * 1e3, 2),
+        },
+        "prefill": {
+            "value": round(prefill_tflops, 2),
+            "unit": "TFLOP/s",
+            "flops_per_launch": pf_flops,
+            "avg_launch_us": round(pf_call_ms * 1e3, 2),
+            "store_plus_prefill_us": round(float(np.mean(pf_ms)) * 1e3, 2),
+            "roofline": {"bound": "mfma", "achieved": round(prefill_tflops, 2),
+                         "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(prefill_tflops / MFMA_BF16_PEAK_TFLOPS, 4)},
+        },
+        "cpu_baseline": cpu,
+        "host_wall_s": round(wall, 3),
+    }
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(lay, k_pool, v_pool, q, target_s=12.0):
+    """The fp64 oracle on host cores over a bounded sample of the decode
+    workload: layer 0, the first n sequences (all 16 heads), n sized from a
+    short probe so the sample takes about target_s seconds."""
+    import torch
+
+    import oracle
+
+    def bits(t):
+        return t.cpu().view(torch.int16).numpy().view(np.uint16)
+
+    kp, vp, qh = bits(k_pool), bits(v_pool), bits(q)
+    probe = np.arange(8, dtype=np.int32)
+    t0 = time.perf_counter()
+    oracle.decode(qh, kp, vp, lay.context_lens, lay.block_table, lay.scale, seqs=probe)
+    per_seq = (time.perf_counter() - t0) / len(probe)
+    n_seqs = int(min(lay.num_seqs, max(8, target_s / max(per_seq, 1e-6))))
+    seqs = np.arange(n_seqs, dtype=np.int32)
+    t0 = time.perf_counter()
+    oracle.decode(qh, kp, vp, lay.context_lens, lay.block_table, lay.scale, seqs=seqs)
+    dt = time.perf_counter() - t0
+    kv = int(lay.context_lens[:n_seqs].astype(np.int64).sum()) * lay.num_kv_heads * lay.head_dim * 2 * 2
+    return {"value": round(kv / dt / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": (f"decode layer 0, first {n_seqs} of {lay.num_seqs} sequences, all "
+                       f"{lay.num_q_heads} query heads: {kv} KV bytes in {dt:.2f} s")}
+
+
+if __name__ == "__main__":
+    main()

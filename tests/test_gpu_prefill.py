@@ -100,6 +100,8 @@ def test_c5a_mixed_chunked_sampled_rows():
 @pytest.mark.parametrize("dtype,d,hq,hkv,bs", [
     ("bf16", 128, 16, 8, 16), ("bf16", 64, 8, 1, 32), ("bf16", 128, 4, 4, 1), ("bf16", 32, 4, 2, 16),
     ("bf16", 256, 4, 2, 16), ("f32", 128, 8, 2, 16), ("f32", 64, 8, 8, 4), ("bf16", 128, 32, 4, 64),
+    ("bf16", 128, 8, 8, 16), ("bf16", 128, 16, 8, 4), ("bf16", 64, 16, 4, 8), ("bf16", 128, 16, 8, 256),
+    ("bf16", 64, 4, 1, 2048),
 ])
 def test_ragged_shapes_and_offsets(dtype, d, hq, hkv, bs):
     """Ragged lengths spanning several tiles plus tails, arbitrary cached
