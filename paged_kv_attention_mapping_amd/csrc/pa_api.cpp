@@ -49,6 +49,7 @@ pa_status check_attention_shape(const pa_pool *pool, int32_t num_q_heads, pa::Po
     const int group = num_q_heads / g->hkv;
     if (group != 1 && group != 2 && group != 4 && group != 8) return PA_ERR_UNSUPPORTED;
     if (g->d != 32 && g->d != 64 && g->d != 128 && g->d != 256) return PA_ERR_UNSUPPORTED;
+    if (g->num_blocks < 1) return PA_ERR_BAD_SHAPE;  // attention needs a non-empty pool
     return PA_OK;
 }
 

@@ -16,10 +16,12 @@
 // (bf16, d=128: 16 lanes x 16 B = 256 B per token, 4 tokens per wave).  The G
 // query heads that share KV head g are all served from the same K/V bytes
 // (GQA reuse, fork Q&A Q3 section 2), so every K/V byte is read from HBM once.
-// Scores are reduced across the LPT lanes with DPP row operations.  Phase 1
-// streams K and writes scores (pre-multiplied by scale*log2 e) to LDS;
-// phase 2 takes the split's max; phase 3 streams V, accumulating
-// exp2(s - m) * v.  Block ids of a split are staged in LDS once.
+// One pass: each round a lane issues all its K and V loads together (8 + 8
+// 16-byte loads in flight), the scores are summed across the LPT lanes with
+// DPP row operations (bf16 q.k on v_dot2_f32_bf16), and a running max,
+// normaliser and fp32 accumulator per lane group absorb the round (online
+// softmax in the log2 domain).  The groups of a wave and then the waves are
+// combined by log-sum-exp.  Block ids of a split are staged in LDS once.
 //
 // The same kernel also serves as the vector-ALU prefill path: a prefill row is
 // one packed query token whose context is min(q_offset + i + 1, k_len) keys.
@@ -33,7 +35,7 @@ namespace {
 
 constexpr int kNW = 4;        // waves per workgroup
 constexpr int kThreads = kNW * kWave;
-constexpr int kUnroll = 8;    // 16-byte loads in flight per lane per phase
+constexpr int kUnroll = 4;    // tokens per lane per round (K and V loads each)
 constexpr int kSplitMax = 1024;  // keys per split, upper bound
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -93,14 +95,48 @@ struct RowArgs {
     float *ws_l;
 };
 
+// This lane's slice of one query head, kept in the form the dot product wants:
+// bf16 stays packed (two elements per 32-bit word, consumed by v_dot2_f32_bf16);
+// fp32 is kept as floats.
+template <typename T> struct QSlice;
+template <> struct QSlice<bf16_t> {
+    uint4 w;
+    __device__ __forceinline__ void load(const bf16_t *p) { w = ld16(p); }
+    __device__ __forceinline__ float dot(const uint4 &k) const {
+        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+        float acc = 0.f;
+        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w.x), __builtin_bit_cast(bf16x2, k.x), acc, false);
+        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w.y), __builtin_bit_cast(bf16x2, k.y), acc, false);
+        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w.z), __builtin_bit_cast(bf16x2, k.z), acc, false);
+        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w.w), __builtin_bit_cast(bf16x2, k.w), acc, false);
+        return acc;
+    }
+};
+template <> struct QSlice<float> {
+    float f[4];
+    __device__ __forceinline__ void load(const float *p) { unpack16<float>(ld16(p), f); }
+    __device__ __forceinline__ float dot(const uint4 &k) const {
+        float kf[4];
+        unpack16<float>(k, kf);
+        float acc = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc = fmaf(f[e], kf[e], acc);
+        return acc;
+    }
+};
+
+// One pass over the split's keys with an online softmax kept per lane group:
+// every round each lane issues kUnroll K loads and kUnroll V loads at once,
+// scores them (DPP sum over the LPT lanes of a token), rescales its running
+// (m, l, acc) once per round and accumulates p * v.  At the end the token
+// groups of a wave and then the waves are combined by log-sum-exp.
 template <typename T, int D, int G, class Rows>
 __global__ __launch_bounds__(kThreads) void row_attn_split(RowArgs a, Rows rows) {
     using C = RowCfg<T, D>;
     constexpr int EPV = C::EPV, LPT = C::LPT, TPW = C::TPW, TPR = C::TPR;
-    static_assert(kNW * D <= kSplitMax, "accumulator staging aliases the score buffer");
-    __shared__ float s_buf[G * kSplitMax];   // scores [G][split], later [kNW][G][D]
     __shared__ int s_blk[kSplitMax];         // physical block ids of this split
-    __shared__ float s_l[kNW][G];
+    __shared__ float s_acc[kNW][G][D];
+    __shared__ float s_m[kNW][G], s_l[kNW][G];
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1), w = tid >> 6;
@@ -126,7 +162,6 @@ __global__ __launch_bounds__(kThreads) void row_attn_split(RowArgs a, Rows rows)
         return;
     }
     const int t1 = min(t0 + a.split_tokens, ctx);
-    const int n = t1 - t0;
     const int nsplit_row = (ctx + a.split_tokens - 1) / a.split_tokens;
     const int shift = a.block_shift;
     const int bmask = (1 << shift) - 1;
@@ -140,133 +175,132 @@ __global__ __launch_bounds__(kThreads) void row_attn_split(RowArgs a, Rows rows)
             s_blk[i] = (p >= 0 && (int64_t)p < a.num_blocks) ? p : -1;
         }
     }
-
-    // this lane's slice of the G query heads, pre-scaled by scale*log2(e)
-    float qv[G][EPV];
+    QSlice<T> qv[G];
     {
         const T *qrow = reinterpret_cast<const T *>(a.q) + (int64_t)row * a.q_row_stride + (int64_t)g * G * D;
 #pragma unroll
-        for (int j = 0; j < G; ++j) {
-            unpack16<T>(ld16(qrow + j * D + c * EPV), qv[j]);
-#pragma unroll
-            for (int e = 0; e < EPV; ++e) qv[j][e] *= a.scale_log2;
-        }
+        for (int j = 0; j < G; ++j) qv[j].load(qrow + j * D + c * EPV);
     }
     __syncthreads();
 
     const T *kp = reinterpret_cast<const T *>(a.k_pool);
     const T *vp = reinterpret_cast<const T *>(a.v_pool);
     const int64_t head_off = (int64_t)g * D + c * EPV;
+    const int64_t slot_stride = (int64_t)hkv * D;
 
-    // ---- phase 1: scores -------------------------------------------------
-    for (int base = t0; base < t1; base += TPR) {
-        uint4 kr[kUnroll];
-        unsigned valid = 0;
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const int tok = base + (u * kNW + w) * TPW + tg;
-            int p = -1;
-            if (tok < t1) p = s_blk[(tok >> shift) - b0];
-            if (p >= 0) {
-                const int64_t slot = ((int64_t)p << shift) + (tok & bmask);
-                kr[u] = ld16(kp + slot * hkv * D + head_off);
-                valid |= 1u << u;
-            } else {
-                kr[u] = make_uint4(0, 0, 0, 0);
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const int tok = base + (u * kNW + w) * TPW + tg;
-            float kf[EPV];
-            unpack16<T>(kr[u], kf);
-#pragma unroll
-            for (int j = 0; j < G; ++j) {
-                float dot = 0.f;
-#pragma unroll
-                for (int e = 0; e < EPV; ++e) dot = fmaf(qv[j][e], kf[e], dot);
-                dot = group_sum<LPT>(dot);
-                if (c == 0 && tok < t1) s_buf[j * kSplitMax + (tok - t0)] = ((valid >> u) & 1) ? dot : -INFINITY;
-            }
-        }
-    }
-    __syncthreads();
-
-    // ---- phase 2: split max per head (every wave computes the same value) --
-    float m[G];
+    float m[G], l[G], acc[G][EPV];
 #pragma unroll
     for (int j = 0; j < G; ++j) {
-        float x = -INFINITY;
-        for (int i = lane; i < n; i += kWave) x = fmaxf(x, s_buf[j * kSplitMax + i]);
-        x = group_max<kWave>(x);
-        m[j] = (x == -INFINITY) ? 0.f : x;
-    }
-
-    // ---- phase 3: exp2(s - m) * v ------------------------------------------
-    float acc[G][EPV];
-    float l[G];
-#pragma unroll
-    for (int j = 0; j < G; ++j) {
+        m[j] = -INFINITY;
         l[j] = 0.f;
 #pragma unroll
         for (int e = 0; e < EPV; ++e) acc[j][e] = 0.f;
     }
-    for (int base = t0; base < t1; base += TPR) {
-        uint4 vr[kUnroll];
+
+    // Software pipeline over rounds of TPR tokens: the loads of round r+1 are
+    // issued before round r is scored, from two register buffers.  Tokens past
+    // t1 (and ids outside the pool) are masked; their loads all hit slot 0 of
+    // the pool, one cached line, so the trailing prefetch costs no HBM traffic.
+    auto issue = [&](uint4 (&kr)[kUnroll], uint4 (&vr)[kUnroll], int (&blk)[kUnroll], int base) {
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
             const int tok = base + (u * kNW + w) * TPW + tg;
-            int p = -1;
-            if (tok < t1) p = s_blk[(tok >> shift) - b0];
-            if (p >= 0) {
-                const int64_t slot = ((int64_t)p << shift) + (tok & bmask);
-                vr[u] = ld16(vp + slot * hkv * D + head_off);
-            } else {
-                vr[u] = make_uint4(0, 0, 0, 0);
-            }
+            blk[u] = tok < t1 ? s_blk[(tok >> shift) - b0] : -1;
         }
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
             const int tok = base + (u * kNW + w) * TPW + tg;
-            if (tok < t1) {
-                float vf[EPV];
-                unpack16<T>(vr[u], vf);
+            const int64_t slot = blk[u] >= 0 ? ((int64_t)blk[u] << shift) + (tok & bmask) : 0;
+            kr[u] = ld16_stream(kp + slot * slot_stride + head_off);
+            vr[u] = ld16_stream(vp + slot * slot_stride + head_off);
+        }
+    };
+    auto consume = [&](const uint4 (&kr)[kUnroll], const uint4 (&vr)[kUnroll], const int (&blk)[kUnroll]) {
+        float sc[kUnroll][G];
 #pragma unroll
-                for (int j = 0; j < G; ++j) {
-                    const float pj = exp2f(s_buf[j * kSplitMax + (tok - t0)] - m[j]);
-                    l[j] += pj;
+        for (int u = 0; u < kUnroll; ++u)
 #pragma unroll
-                    for (int e = 0; e < EPV; ++e) acc[j][e] = fmaf(pj, vf[e], acc[j][e]);
-                }
+            for (int j = 0; j < G; ++j) {
+                const float dot = group_sum<LPT>(qv[j].dot(kr[u]));
+                sc[u][j] = blk[u] >= 0 ? dot * a.scale_log2 : -INFINITY;
             }
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            float mx = m[j];
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) mx = fmaxf(mx, sc[u][j]);
+            const float m_use = (mx == -INFINITY) ? 0.f : mx;
+            const float alpha = exp2f(m[j] - m_use);
+            m[j] = mx;
+            float ps = 0.f;
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                sc[u][j] = exp2f(sc[u][j] - m_use);
+                ps += sc[u][j];
+            }
+            l[j] = l[j] * alpha + ps;
+#pragma unroll
+            for (int e = 0; e < EPV; ++e) acc[j][e] *= alpha;
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            float vf[EPV];
+            unpack16<T>(blk[u] >= 0 ? vr[u] : make_uint4(0, 0, 0, 0), vf);
+#pragma unroll
+            for (int j = 0; j < G; ++j)
+#pragma unroll
+                for (int e = 0; e < EPV; ++e) acc[j][e] = fmaf(sc[u][j], vf[e], acc[j][e]);
+        }
+    };
+    {
+        uint4 kA[kUnroll], vA[kUnroll], kB[kUnroll], vB[kUnroll];
+        int bA[kUnroll], bB[kUnroll];
+        issue(kA, vA, bA, t0);
+        for (int base = t0; base < t1; base += 2 * TPR) {
+            issue(kB, vB, bB, base + TPR);
+            consume(kA, vA, bA);
+            if (base + TPR >= t1) break;
+            issue(kA, vA, bA, base + 2 * TPR);
+            consume(kB, vB, bB);
         }
     }
 
-    // ---- reduce over the token groups of a wave, then over waves ----------
+    // ---- combine the token groups of the wave (lanes sharing c) -----------
 #pragma unroll
     for (int j = 0; j < G; ++j) {
-        l[j] = cross_group_sum<LPT>(l[j]);
+        float M = m[j];
 #pragma unroll
-        for (int e = 0; e < EPV; ++e) acc[j][e] = cross_group_sum<LPT>(acc[j][e]);
+        for (int sft = LPT; sft < kWave; sft <<= 1) M = fmaxf(M, __shfl_xor(M, sft));
+        const float f = (m[j] == -INFINITY) ? 0.f : exp2f(m[j] - M);
+        l[j] = cross_group_sum<LPT>(l[j] * f);
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) acc[j][e] = cross_group_sum<LPT>(acc[j][e] * f);
+        m[j] = M;
     }
-    __syncthreads();  // every wave is done reading scores; reuse s_buf
-    float *s_acc = s_buf;  // [kNW][G][D]
     if (tg == 0) {
 #pragma unroll
         for (int j = 0; j < G; ++j) {
 #pragma unroll
-            for (int e = 0; e < EPV; ++e) s_acc[(w * G + j) * D + c * EPV + e] = acc[j][e];
-            if (c == 0) s_l[w][j] = l[j];
+            for (int e = 0; e < EPV; ++e) s_acc[w][j][c * EPV + e] = acc[j][e];
+            if (c == 0) {
+                s_m[w][j] = m[j];
+                s_l[w][j] = l[j];
+            }
         }
     }
     __syncthreads();
+    // ---- combine the waves, then write the output or the split's partials --
     for (int i = tid; i < G * D; i += kThreads) {
         const int j = i / D, d = i - j * D;
+        float M = -INFINITY;
+#pragma unroll
+        for (int ww = 0; ww < kNW; ++ww) M = fmaxf(M, s_m[ww][j]);
         float A = 0.f, L = 0.f;
 #pragma unroll
         for (int ww = 0; ww < kNW; ++ww) {
-            A += s_acc[(ww * G + j) * D + d];
-            L += s_l[ww][j];
+            const float f = (s_m[ww][j] == -INFINITY) ? 0.f : exp2f(s_m[ww][j] - M);
+            A += s_acc[ww][j][d] * f;
+            L += s_l[ww][j] * f;
         }
         if (nsplit_row == 1) {
             store_elem<T>(out_row + i, L > 0.f ? A / L : 0.f);
@@ -274,7 +308,7 @@ __global__ __launch_bounds__(kThreads) void row_attn_split(RowArgs a, Rows rows)
             const int64_t idx = ((int64_t)row * hq + g * G + j) * a.num_splits + split;
             a.ws_acc[idx * D + d] = A;
             if (d == 0) {
-                a.ws_m[idx] = m[j];
+                a.ws_m[idx] = M;
                 a.ws_l[idx] = L;
             }
         }
@@ -310,12 +344,16 @@ __global__ __launch_bounds__(kThreads) void row_attn_merge(MergeArgs a, Rows row
     const int64_t base = ((int64_t)row * a.hq + h) * a.num_splits;
     float mstar = -INFINITY;
     for (int s = 0; s < ns; ++s) mstar = fmaxf(mstar, a.ws_m[base + s]);
+    auto weight = [&](int s) {
+        const float ms = a.ws_m[base + s];
+        return ms == -INFINITY ? 0.f : exp2f(ms - mstar);
+    };
     float L = 0.f;
-    for (int s = 0; s < ns; ++s) L += a.ws_l[base + s] * exp2f(a.ws_m[base + s] - mstar);
+    for (int s = 0; s < ns; ++s) L += a.ws_l[base + s] * weight(s);
     T *o = reinterpret_cast<T *>(a.out) + ((int64_t)row * a.hq + h) * D;
     for (int d = lane; d < D; d += kWave) {
         float A = 0.f;
-        for (int s = 0; s < ns; ++s) A += a.ws_acc[(base + s) * D + d] * exp2f(a.ws_m[base + s] - mstar);
+        for (int s = 0; s < ns; ++s) A += a.ws_acc[(base + s) * D + d] * weight(s);
         store_elem<T>(o + d, L > 0.f ? A / L : 0.f);
     }
 }

@@ -84,7 +84,15 @@ template <int STRIDE> __device__ __forceinline__ float cross_group_sum(float x) 
     return x;
 }
 
-// Loads that bypass nothing special: plain 16-byte global loads.
+// Plain 16-byte global load.
 __device__ __forceinline__ uint4 ld16(const void *p) { return *reinterpret_cast<const uint4 *>(p); }
+
+// 16-byte global load marked nontemporal: for data read exactly once (the
+// decode stream of K/V), so it does not displace reusable lines in the caches.
+__device__ __forceinline__ uint4 ld16_stream(const void *p) {
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
 
 }  // namespace pa
