@@ -102,7 +102,7 @@ size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t total_q, int32_t num
     if (num_seqs <= 0 || total_q <= 0) return 0;
     const int group = num_q_heads / g.hkv;
     if (pa::prefill_mfma_supported(g, group)) return 0;
-    const pa::RowAttnPlan plan = pa::plan_row_attention(total_q, g.hkv, g.d, g.dtype, group, max_seqlen_k);
+    const pa::RowAttnPlan plan = pa::plan_row_attention(total_q, g, group, max_seqlen_k);
     return pa::row_attention_workspace_bytes(plan, num_q_heads, g.d);
 }
 
@@ -112,7 +112,7 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
     if (check_attention_shape(pool, num_q_heads, &g) != PA_OK) return 0;
     if (num_seqs <= 0 || max_context_len <= 0) return 0;
     const int group = num_q_heads / g.hkv;
-    const pa::RowAttnPlan plan = pa::plan_row_attention(num_seqs, g.hkv, g.d, g.dtype, group, max_context_len);
+    const pa::RowAttnPlan plan = pa::plan_row_attention(num_seqs, g, group, max_context_len);
     return pa::row_attention_workspace_bytes(plan, num_q_heads, g.d);
 }
 
@@ -143,7 +143,7 @@ pa_status pa_prefill_varlen(const void *q, int64_t q_row_stride, int32_t num_q_h
                                                 block_table_stride, num_seqs, total_q, max_seqlen_q,
                                                 softmax_scale, out, (hipStream_t)stream));
     }
-    const pa::RowAttnPlan plan = pa::plan_row_attention(total_q, g.hkv, g.d, g.dtype, group, max_seqlen_k);
+    const pa::RowAttnPlan plan = pa::plan_row_attention(total_q, g, group, max_seqlen_k);
     const size_t need = pa::row_attention_workspace_bytes(plan, num_q_heads, g.d);
     if (need && (!workspace || workspace_bytes < need)) return PA_ERR_WORKSPACE;
     return from_hip(pa::launch_prefill_rows(q, q_row_stride, num_q_heads, k_pool, v_pool, g,
@@ -169,7 +169,7 @@ pa_status pa_decode(const void *q, int64_t q_row_stride, int32_t num_q_heads, co
     if (!aligned16(q) || (q_row_stride * eb) % 16 || !aligned16(k_pool) || !aligned16(v_pool))
         return PA_ERR_UNSUPPORTED;
     const int group = num_q_heads / g.hkv;
-    const pa::RowAttnPlan plan = pa::plan_row_attention(num_seqs, g.hkv, g.d, g.dtype, group, max_context_len);
+    const pa::RowAttnPlan plan = pa::plan_row_attention(num_seqs, g, group, max_context_len);
     const size_t need = pa::row_attention_workspace_bytes(plan, num_q_heads, g.d);
     if (need && (!workspace || workspace_bytes < need)) return PA_ERR_WORKSPACE;
     return from_hip(pa::launch_decode(q, q_row_stride, num_q_heads, k_pool, v_pool, g, context_lens,

@@ -33,20 +33,20 @@
 namespace pa {
 namespace {
 
-constexpr int kNW = 4;        // waves per workgroup
+constexpr int kNW = 4;        // waves per merge workgroup
 constexpr int kThreads = kNW * kWave;
 constexpr int kUnroll = 4;    // tokens per lane per round (K and V loads each)
-constexpr int kSplitMax = 1024;  // keys per split, upper bound
+constexpr int kSplitMax = 1 << 20;   // keys per split, upper bound
+constexpr int kBlkIds = 4096;        // block ids a split may span (LDS staging)
 constexpr float kLog2e = 1.4426950408889634f;
 
-template <typename T, int D>
+template <typename T, int D, int NW>
 struct RowCfg {
     static constexpr int EPV = 16 / Elem<T>::bytes;  // elements per 16-byte vector
     static constexpr int LPT = D / EPV;              // lanes per token row
     static constexpr int TPW = kWave / LPT;          // tokens per wave per load
-    static constexpr int TPR = kNW * TPW * kUnroll;  // tokens per round
+    static constexpr int TPR = NW * TPW * kUnroll;   // tokens per round
     static_assert(LPT >= 1 && LPT <= kWave && kWave % LPT == 0, "head_dim");
-    static_assert(kSplitMax % TPR == 0, "split");
 };
 
 struct DecodeRows {
@@ -130,13 +130,14 @@ template <> struct QSlice<float> {
 // scores them (DPP sum over the LPT lanes of a token), rescales its running
 // (m, l, acc) once per round and accumulates p * v.  At the end the token
 // groups of a wave and then the waves are combined by log-sum-exp.
-template <typename T, int D, int G, class Rows>
-__global__ __launch_bounds__(kThreads) void row_attn_split(RowArgs a, Rows rows) {
-    using C = RowCfg<T, D>;
+template <typename T, int D, int G, int NW, class Rows>
+__global__ __launch_bounds__(NW * kWave) void row_attn_split(RowArgs a, Rows rows) {
+    using C = RowCfg<T, D, NW>;
     constexpr int EPV = C::EPV, LPT = C::LPT, TPW = C::TPW, TPR = C::TPR;
-    __shared__ int s_blk[kSplitMax];         // physical block ids of this split
-    __shared__ float s_acc[kNW][G][D];
-    __shared__ float s_m[kNW][G], s_l[kNW][G];
+    constexpr int kNW = NW, kThreads = NW * kWave;
+    __shared__ int s_blk[kBlkIds];           // physical block ids of this split
+    __shared__ float s_acc[NW][G][D];
+    __shared__ float s_m[NW][G], s_l[NW][G];
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1), w = tid >> 6;
@@ -329,8 +330,11 @@ struct MergeArgs {
 };
 
 // One wave per (row, query head): out = sum_c acc_c 2^(m_c - m*) / sum_c l_c 2^(m_c - m*).
+// Lane s holds split s's (m, l); the split weights are reduced across the wave
+// and broadcast with shuffles, so the whole merge is one round trip to memory.
 template <typename T, int D, class Rows>
 __global__ __launch_bounds__(kThreads) void row_attn_merge(MergeArgs a, Rows rows) {
+    constexpr int DPL = (D + kWave - 1) / kWave;  // output elements per lane
     const int64_t wave = (int64_t)blockIdx.x * kNW + (threadIdx.x >> 6);
     const int lane = threadIdx.x & (kWave - 1);
     if (wave >= (int64_t)a.num_rows * a.hq) return;
@@ -342,34 +346,55 @@ __global__ __launch_bounds__(kThreads) void row_attn_merge(MergeArgs a, Rows row
     const int ns = (ctx + a.split_tokens - 1) / a.split_tokens;
     if (ns <= 1) return;  // written directly by the split kernel
     const int64_t base = ((int64_t)row * a.hq + h) * a.num_splits;
-    float mstar = -INFINITY;
-    for (int s = 0; s < ns; ++s) mstar = fmaxf(mstar, a.ws_m[base + s]);
-    auto weight = [&](int s) {
-        const float ms = a.ws_m[base + s];
-        return ms == -INFINITY ? 0.f : exp2f(ms - mstar);
-    };
-    float L = 0.f;
-    for (int s = 0; s < ns; ++s) L += a.ws_l[base + s] * weight(s);
     T *o = reinterpret_cast<T *>(a.out) + ((int64_t)row * a.hq + h) * D;
-    for (int d = lane; d < D; d += kWave) {
-        float A = 0.f;
-        for (int s = 0; s < ns; ++s) A += a.ws_acc[(base + s) * D + d] * weight(s);
-        store_elem<T>(o + d, L > 0.f ? A / L : 0.f);
+    float A[DPL];
+#pragma unroll
+    for (int k = 0; k < DPL; ++k) A[k] = 0.f;
+    float L = 0.f;
+    // splits in chunks of 64 (one per lane); the running max rescales earlier chunks
+    float M = -INFINITY;
+    for (int s0 = 0; s0 < ns; s0 += kWave) {
+        const int sl = s0 + lane;
+        const float ms = sl < ns ? a.ws_m[base + sl] : -INFINITY;
+        const float ls = sl < ns ? a.ws_l[base + sl] : 0.f;
+        const float cm = group_max<kWave>(ms);
+        const float Mn = fmaxf(M, cm);
+        if (Mn == -INFINITY) continue;
+        const float r = M == -INFINITY ? 0.f : exp2f(M - Mn);
+        const float wl = ms == -INFINITY ? 0.f : exp2f(ms - Mn);
+        L = L * r + group_sum<kWave>(ls * wl);
+#pragma unroll
+        for (int k = 0; k < DPL; ++k) A[k] *= r;
+        const int cnt = min(kWave, ns - s0);
+        for (int s = 0; s < cnt; ++s) {
+            const float ws = __shfl(wl, s);
+#pragma unroll
+            for (int k = 0; k < DPL; ++k) {
+                const int d = lane + k * kWave;
+                if (d < D) A[k] = fmaf(a.ws_acc[(base + s0 + s) * D + d], ws, A[k]);
+            }
+        }
+        M = Mn;
+    }
+#pragma unroll
+    for (int k = 0; k < DPL; ++k) {
+        const int d = lane + k * kWave;
+        if (d < D) store_elem<T>(o + d, L > 0.f ? A[k] / L : 0.f);
     }
 }
 
-int tokens_per_round(int dtype, int d) {
+int tokens_per_round(int dtype, int d, int nw) {
     const int epv = dtype == 0 ? 4 : 8;
     const int lpt = d / epv;
-    return kNW * (kWave / lpt) * kUnroll;
+    return nw * (kWave / lpt) * kUnroll;
 }
 
-template <typename T, int D, int G, class Rows>
+template <typename T, int D, int G, int NW, class Rows>
 hipError_t run_rows(const RowArgs &a, const Rows &rows, hipStream_t stream) {
     const int64_t wgs = (int64_t)a.num_rows * a.num_splits * a.hkv;
     if (wgs == 0) return hipSuccess;
-    hipLaunchKernelGGL((row_attn_split<T, D, G, Rows>), dim3((unsigned)wgs), dim3(kThreads), 0, stream,
-                       a, rows);
+    hipLaunchKernelGGL((row_attn_split<T, D, G, NW, Rows>), dim3((unsigned)wgs), dim3(NW * kWave), 0,
+                       stream, a, rows);
     if (a.num_splits > 1) {
         MergeArgs m{a.num_rows, a.hkv * G, a.num_splits, a.split_tokens, a.bt_stride, a.block_shift,
                     a.ws_acc, a.ws_m, a.ws_l, a.out};
@@ -380,32 +405,43 @@ hipError_t run_rows(const RowArgs &a, const Rows &rows, hipStream_t stream) {
     return hipGetLastError();
 }
 
+template <typename T, int D, int G, class Rows>
+hipError_t dispatch_waves(int waves, const RowArgs &a, const Rows &rows, hipStream_t s) {
+    if constexpr (G <= 2) {  // wider workgroups only where the registers allow them
+        if (waves == 16) return run_rows<T, D, G, 16>(a, rows, s);
+        if (waves == 8) return run_rows<T, D, G, 8>(a, rows, s);
+    }
+    if (waves == 4) return run_rows<T, D, G, 4>(a, rows, s);
+    return hipErrorInvalidValue;
+}
+
 template <typename T, int D, class Rows>
-hipError_t dispatch_group(int group, const RowArgs &a, const Rows &rows, hipStream_t s) {
+hipError_t dispatch_group(int group, int waves, const RowArgs &a, const Rows &rows, hipStream_t s) {
     switch (group) {
-        case 1: return run_rows<T, D, 1>(a, rows, s);
-        case 2: return run_rows<T, D, 2>(a, rows, s);
-        case 4: return run_rows<T, D, 4>(a, rows, s);
-        case 8: return run_rows<T, D, 8>(a, rows, s);
+        case 1: return dispatch_waves<T, D, 1>(waves, a, rows, s);
+        case 2: return dispatch_waves<T, D, 2>(waves, a, rows, s);
+        case 4: return dispatch_waves<T, D, 4>(waves, a, rows, s);
+        case 8: return dispatch_waves<T, D, 8>(waves, a, rows, s);
     }
     return hipErrorInvalidValue;
 }
 
 template <typename T, class Rows>
-hipError_t dispatch_dim(int d, int group, const RowArgs &a, const Rows &rows, hipStream_t s) {
+hipError_t dispatch_dim(int d, int group, int waves, const RowArgs &a, const Rows &rows, hipStream_t s) {
     switch (d) {
-        case 32: return dispatch_group<T, 32>(group, a, rows, s);
-        case 64: return dispatch_group<T, 64>(group, a, rows, s);
-        case 128: return dispatch_group<T, 128>(group, a, rows, s);
-        case 256: return dispatch_group<T, 256>(group, a, rows, s);
+        case 32: return dispatch_group<T, 32>(group, waves, a, rows, s);
+        case 64: return dispatch_group<T, 64>(group, waves, a, rows, s);
+        case 128: return dispatch_group<T, 128>(group, waves, a, rows, s);
+        case 256: return dispatch_group<T, 256>(group, waves, a, rows, s);
     }
     return hipErrorInvalidValue;
 }
 
 template <class Rows>
-hipError_t dispatch(const PoolGeom &g, int group, const RowArgs &a, const Rows &rows, hipStream_t s) {
-    return g.dtype == 0 ? dispatch_dim<float>(g.d, group, a, rows, s)
-                        : dispatch_dim<bf16_t>(g.d, group, a, rows, s);
+hipError_t dispatch(const PoolGeom &g, int group, int waves, const RowArgs &a, const Rows &rows,
+                    hipStream_t s) {
+    return g.dtype == 0 ? dispatch_dim<float>(g.d, group, waves, a, rows, s)
+                        : dispatch_dim<bf16_t>(g.d, group, waves, a, rows, s);
 }
 
 RowArgs make_args(const void *q, int64_t q_row_stride, int hq, const void *k_pool, const void *v_pool,
@@ -438,17 +474,34 @@ RowArgs make_args(const void *q, int64_t q_row_stride, int hq, const void *k_poo
 
 }  // namespace
 
-RowAttnPlan plan_row_attention(int num_rows, int hkv, int d, int dtype, int group, int max_keys) {
-    (void)group;
-    RowAttnPlan p{num_rows, 1, kSplitMax};
+RowAttnPlan plan_row_attention(int num_rows, const PoolGeom &g, int group, int max_keys) {
+    // Waves per workgroup: 8 when the per-lane state of the G heads stays
+    // within 128 registers (G <= 2; two 512-thread workgroups per CU), else 4.
+    // Wider workgroups stream one (row, KV head) faster, which shortens the
+    // tail when context lengths are ragged; two per CU keep one streaming
+    // while the other starts up or reduces.
+    int waves = group <= 2 ? 8 : 4;
+#ifdef PA_WAVES_OVERRIDE
+    waves = PA_WAVES_OVERRIDE;
+#endif
+    RowAttnPlan p{num_rows, 1, 1, waves};
     if (num_rows <= 0 || max_keys <= 0) return p;
-    const int tpr = tokens_per_round(dtype, d);
-    const int64_t target_wgs = 2048;  // ~8 workgroups per CU on 256 CUs
-    int split = kSplitMax;
-    auto wgs = [&](int s) { return (int64_t)num_rows * hkv * ((max_keys + s - 1) / s); };
+    const int tpr = tokens_per_round(g.dtype, g.d, waves);
+    const int64_t slots = 256LL * 16 / waves;        // resident workgroups on 256 CUs
+    const int64_t target_wgs = 2 * slots;
+    const int64_t units = (int64_t)num_rows * g.hkv;
+    // a split covers at most kBlkIds blocks (LDS staging of its block ids)
+    const int64_t cap = min((int64_t)kSplitMax, (int64_t)kBlkIds << g.block_shift);
+    int64_t split = tpr;
+    while (split < max_keys && split < cap) split <<= 1;
+    split = min(split, cap);
+    auto wgs = [&](int64_t sp) { return units * ((max_keys + sp - 1) / sp); };
     while (split > tpr && wgs(split) < target_wgs) split >>= 1;
-    p.split_tokens = split;
-    p.num_splits = (max_keys + split - 1) / split;
+#ifdef PA_SPLIT_OVERRIDE
+    split = min((int64_t)PA_SPLIT_OVERRIDE, cap);
+#endif
+    p.split_tokens = (int)split;
+    p.num_splits = (int)((max_keys + split - 1) / split);
     return p;
 }
 
@@ -464,7 +517,7 @@ hipError_t launch_decode(const void *q, int64_t q_row_stride, int hq, const void
                          float softmax_scale, void *out, void *workspace, hipStream_t stream) {
     const RowArgs a = make_args(q, q_row_stride, hq, k_pool, v_pool, g, block_table, bt_stride, plan,
                                 softmax_scale, out, workspace);
-    return dispatch(g, hq / g.hkv, a, DecodeRows{context_lens}, stream);
+    return dispatch(g, hq / g.hkv, plan.waves, a, DecodeRows{context_lens}, stream);
 }
 
 hipError_t launch_prefill_rows(const void *q, int64_t q_row_stride, int hq, const void *k_pool,
@@ -475,8 +528,8 @@ hipError_t launch_prefill_rows(const void *q, int64_t q_row_stride, int hq, cons
                                void *workspace, hipStream_t stream) {
     const RowArgs a = make_args(q, q_row_stride, hq, k_pool, v_pool, g, block_table, bt_stride, plan,
                                 softmax_scale, out, workspace);
-    return dispatch(g, hq / g.hkv, a, PrefillRows{cu_seqlens_q, cu_seqlens_k, q_offsets, num_seqs},
-                    stream);
+    return dispatch(g, hq / g.hkv, plan.waves, a,
+                    PrefillRows{cu_seqlens_q, cu_seqlens_k, q_offsets, num_seqs}, stream);
 }
 
 }  // namespace pa

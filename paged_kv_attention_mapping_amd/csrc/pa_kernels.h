@@ -35,11 +35,11 @@ struct RowAttnPlan {
     int num_rows;
     int num_splits;     // splits per row (grid dimension)
     int split_tokens;   // keys per split
+    int waves;          // waves per workgroup
 };
 
 // Splits are chosen from host sizes only, so workspace size and launch agree.
-RowAttnPlan plan_row_attention(int num_rows, int hkv, int d, int dtype, int group,
-                               int max_keys);
+RowAttnPlan plan_row_attention(int num_rows, const PoolGeom &g, int group, int max_keys);
 size_t row_attention_workspace_bytes(const RowAttnPlan &p, int hq, int d);
 
 hipError_t launch_decode(const void *q, int64_t q_row_stride, int hq, const void *k_pool,
