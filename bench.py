@@ -190,7 +190,7 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(kv_bytes_layer / (dec_call_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-            "traffic": None,
+            "traffic": measured_traffic("decode"),
             "bytes_per_launch": kv_bytes_layer,
             "avg_launch_us": round(dec_call_ms * 1e3, 2),
         },
@@ -202,12 +202,31 @@ def main():
             "store_plus_prefill_us": round(float(np.mean(pf_ms)) * 1e3, 2),
             "roofline": {"bound": "mfma", "achieved": round(prefill_tflops, 2),
                          "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(prefill_tflops / MFMA_BF16_PEAK_TFLOPS, 4)},
+                         "frac": round(prefill_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                         "traffic": measured_traffic("prefill")},
         },
         "cpu_baseline": cpu,
         "host_wall_s": round(wall, 3),
     }
     print(json.dumps(result), flush=True)
+
+
+def measured_traffic(which):
+    """HBM bytes per launch (read + write) of the decode or prefill kernel, from
+    the rocprofv3 FETCH_SIZE / WRITE_SIZE runs summarised in profiles/ (scaled by
+    the plain-copy calibration there).  None when the kernel source changed
+    since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path)).get(which)
+    if not rec:
+        return None
+    src = os.path.join(ROOT, rec["source"])
+    if hashlib.sha256(open(src, "rb").read()).hexdigest() != rec["sha256"]:
+        return None
+    return int(rec["read_bytes"] + rec["write_bytes"])
 
 
 def cpu_baseline(lay, k_pool, v_pool, q, target_s=12.0):
