@@ -54,6 +54,13 @@ def build(verbose: bool = False) -> str:
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
+    # A kernel whose host-side instantiation is rejected leaves its launch stub
+    # undefined in the library instead of failing the compile: refuse that.
+    nm = subprocess.run(["nm", "-D", "--undefined-only", tmp], capture_output=True, text=True)
+    missing = [ln.split()[-1] for ln in nm.stdout.splitlines() if "__device_stub__" in ln]
+    if missing:
+        os.remove(tmp)
+        raise RuntimeError(f"libpa.so would have undefined kernel stubs: {missing}")
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}")

@@ -27,16 +27,22 @@
 //    (lane half h, register r -> row 8*(r/4) + 4h + r%4) this puts the scores
 //    of keys 16s + 8h + (0..7) in registers 8s..8s+7 of lane half h, which is
 //    exactly the B operand layout of O^T = V^T . P^T: P never leaves registers.
-//  * V is written to LDS transposed (V^T[d][key]) so the A operand of the PV
-//    product is one 16-byte LDS read per lane.
+//  * K and V tiles go from HBM/L2 straight into LDS (16-byte direct loads, no
+//    staging registers), row-major with a 16-byte XOR swizzle per row, so both
+//    the K reads (ds_read_b128) and the V^T reads are free of bank conflicts.
+//  * the A operand of the PV product, V^T, is read with the gfx950 LDS
+//    transpose load ds_read_b64_tr_b16: in each 16-lane group, lane i gets
+//    element i%4 of the 8-byte chunks named by lanes 4r + i/4 (r = 0..3), so
+//    if lane 4r+q names V[key_r][d0 + 4q] it receives V[key_0..3][d0 + i].
 //  * a workgroup processes a PAIR of query tiles of one sequence, tile p and
 //    tile T-1-p, so every workgroup of a sequence does the same causal work.
 //  * the KV head index varies fastest across workgroups; with 8 KV heads and
 //    workgroups dealt round-robin to the 8 XCDs, all tiles of one KV head run
 //    on one XCD and re-read its K/V from that XCD's L2.
-//  * K/V tiles are double-buffered in LDS: the global loads of tile j+1 are in
+//  * K/V tiles are double-buffered in LDS: the direct loads of tile j+1 are in
 //    flight while tile j is computed.  Block ids are staged in LDS per window.
-//  * rows past k_len are zero-filled, so masked probabilities (0) never meet
+//  * rows a tile holds past the last needed key are loaded from the sequence's
+//    key 0 (finite data), so masked probabilities (exact zeros) never meet
 //    uninitialised pool contents (0 * NaN).
 #include <math.h>
 
@@ -47,12 +53,16 @@ namespace pa {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kPfThreads = 256;
 constexpr int kBN = 64;       // keys per tile
 constexpr int kBlkWin = 1024;  // block ids staged in LDS at a time
 constexpr float kLog2eF = 1.4426950408889634f;
+constexpr float kRescaleLog2 = 8.f;  // lazy-rescale threshold (log2 units)
 
 template <int D, int NH>
 struct Pf {
@@ -60,13 +70,11 @@ struct Pf {
     static constexpr int BM = 32 * SUB;                    // positions per workgroup tile
     static constexpr int KS = D / 16;                      // MFMA k-steps over head_dim
     static constexpr int DT = D / 32;                      // 32-wide output tiles over head_dim
-    static constexpr int KLD = D + 8;                      // LDS row stride (elements), K tile
-    static constexpr int VLD = kBN + 8;                    // LDS row stride (elements), V^T tile
-    static constexpr int CPR = D / 8;                      // 16-byte chunks per K row
-    static constexpr int KCH = kBN * CPR / kPfThreads;     // K chunks per thread
-    static constexpr int VIT = (D / 4) * (kBN / 4);        // 4 keys x 4 dims items per V tile
-    static constexpr int VPT = (VIT + kPfThreads - 1) / kPfThreads;
-    static_assert(KCH >= 1 && kBN * CPR % kPfThreads == 0, "K tile split");
+    static constexpr int CPR = D / 8;                      // 16-byte chunks per row
+    static constexpr int ROWB = D * 2;                     // bytes per LDS row (bf16)
+    static constexpr int TILEB = kBN * ROWB;               // bytes per K or V tile
+    static constexpr int LPW = TILEB / (kPfThreads * 16);  // direct 16-byte loads per lane per tile
+    static_assert(LPW >= 1 && TILEB % (kPfThreads * 16) == 0, "tile split");
 };
 
 struct PfArgs {
@@ -93,22 +101,48 @@ __device__ __forceinline__ int swap_bits_2_3(int i) {
     return (i & ~0xC) | ((i & 4) << 1) | ((i & 8) >> 1);
 }
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
-}
+// 16-byte slot of logical chunk c in LDS row r: K rows use r, V rows use 2r
+// (the transpose reads touch 4 consecutive rows x 2 adjacent chunks).
+template <int CPR> __device__ __forceinline__ int k_slot(int r, int c) { return c ^ (r & (CPR - 1)); }
+template <int CPR> __device__ __forceinline__ int v_slot(int r, int c) { return c ^ ((2 * r) & (CPR - 1)); }
 
-template <int D, int NH>
-struct Tile {
-    using C = Pf<D, NH>;
-    uint4 kreg[C::KCH];
-    uint2 vreg[C::VPT][4];
-};
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// Direct HBM/L2 -> LDS loads of one K tile and one V tile (kBN keys x D).
+// Slot q of a tile (16 bytes) is written by lane q%64 of wave-instruction q/64
+// and holds chunk (slot ^ swizzle) of row q / CPR.  Keys past kmax (masked for
+// every row; their blocks are not staged) and keys in blocks outside the pool
+// are read from key 0 of the sequence (blk0) instead: finite data that the
+// zero probabilities cancel.
+template <class C>
+__device__ __forceinline__ void load_kv_tile(const PfArgs &a, int kb, int kmax, int shift, int bmask,
+                                             int win0, int blk0, int64_t kv_row, int64_t kv_head,
+                                             int w, int lane, const int *s_blk, unsigned char *dk,
+                                             unsigned char *dv) {
+#pragma unroll
+    for (int u = 0; u < C::LPW; ++u) {
+        const int blk_i = w * C::LPW + u;  // 1 KiB block of the tile
+        const int q = blk_i * 64 + lane;
+        const int r = q / C::CPR, sl = q % C::CPR;
+        const int key = kb + r;
+        const int p = key <= kmax ? s_blk[(key >> shift) - win0] : -1;
+        const int64_t slot = p >= 0 ? ((int64_t)p << shift) + (key & bmask)
+                                    : (blk0 >= 0 ? ((int64_t)blk0 << shift) : 0);
+        const int64_t eoff = slot * kv_row + kv_head;
+        __builtin_amdgcn_global_load_lds(a.k_pool + eoff + k_slot<C::CPR>(r, sl) * 8, dk + blk_i * 1024,
+                                         16, 0, 0);
+        __builtin_amdgcn_global_load_lds(a.v_pool + eoff + v_slot<C::CPR>(r, sl) * 8, dv + blk_i * 1024,
+                                         16, 0, 0);
+    }
+}
 
 template <int D, int NH>
 __global__ __launch_bounds__(kPfThreads, 1) void prefill_mfma_kernel(PfArgs a) {
     using C = Pf<D, NH>;
-    __shared__ __attribute__((aligned(16))) uint16_t s_k[2][kBN * C::KLD];
-    __shared__ __attribute__((aligned(16))) uint16_t s_v[2][D * C::VLD];
+    __shared__ __attribute__((aligned(1024))) unsigned char s_k[2][C::TILEB];
+    __shared__ __attribute__((aligned(1024))) unsigned char s_v[2][C::TILEB];
     __shared__ int s_blk[kBlkWin];
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -140,6 +174,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_mfma_kernel(PfArgs a) {
     const float c = a.scale_log2;
     const int64_t kv_row = (int64_t)a.hkv * D;      // elements per pool slot
     const int64_t kv_head = (int64_t)g * D;
+    const int pn = swap_bits_2_3(n);
 
     for (int it = 0; it < 2; ++it) {
         const int tile = it == 0 ? T - 1 - pair : pair;
@@ -192,76 +227,24 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_mfma_kernel(PfArgs a) {
                 s_blk[i] = (p >= 0 && (int64_t)p < a.num_blocks) ? p : -1;
             }
         };
-        // keys past kmax_wg are masked for every row and their blocks are not staged
-        auto blk_of = [&](int key) -> int {
-            return key <= kmax_wg ? s_blk[(key >> shift) - win0] : -1;
-        };
+        // Keys past kmax_wg (masked for every row; their blocks are not staged)
+        // and keys in blocks outside the pool are read from key 0 of the
+        // sequence instead: finite data that the zero probabilities cancel.
+        int blk0 = -1;  // physical block of key 0 (finite stand-in for masked rows)
 
-        Tile<D, NH> reg;
-        auto load_tile = [&](int kt) {
-            const int kb = kt * kBN;
-#pragma unroll
-            for (int ci = 0; ci < C::KCH; ++ci) {
-                const int qi = tid + kPfThreads * ci;
-                const int key = kb + qi / C::CPR, ch = qi % C::CPR;
-                const int p = blk_of(key);
-                reg.kreg[ci] = p >= 0 ? ld16(a.k_pool + (((int64_t)p << shift) + (key & bmask)) * kv_row +
-                                                 kv_head + ch * 8)
-                                      : make_uint4(0, 0, 0, 0);
-            }
-#pragma unroll
-            for (int vi = 0; vi < C::VPT; ++vi) {
-                const int item = tid + kPfThreads * vi;
-                const int dg = item % (D / 4), kg = item / (D / 4);
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk) {
-                    const int key = kb + 4 * kg + kk;
-                    const int p = (item < C::VIT) ? blk_of(key) : -1;
-                    reg.vreg[vi][kk] =
-                        p >= 0 ? *reinterpret_cast<const uint2 *>(
-                                     a.v_pool + (((int64_t)p << shift) + (key & bmask)) * kv_row + kv_head + 4 * dg)
-                               : make_uint2(0, 0);
-                }
-            }
-        };
-        auto store_tile = [&](int buf) {
-#pragma unroll
-            for (int ci = 0; ci < C::KCH; ++ci) {
-                const int qi = tid + kPfThreads * ci;
-                const int key = qi / C::CPR, ch = qi % C::CPR;
-                *reinterpret_cast<uint4 *>(&s_k[buf][key * C::KLD + ch * 8]) = reg.kreg[ci];
-            }
-#pragma unroll
-            for (int vi = 0; vi < C::VPT; ++vi) {
-                const int item = tid + kPfThreads * vi;
-                if (item < C::VIT) {
-                    const int dg = item % (D / 4), kg = item / (D / 4);
-                    const uint2 *x = reg.vreg[vi];
-                    // 4 keys x 4 dims -> for each dim, 4 consecutive keys (8 bytes)
-                    const uint2 d0 = make_uint2((x[0].x & 0xffffu) | (x[1].x << 16),
-                                                (x[2].x & 0xffffu) | (x[3].x << 16));
-                    const uint2 d1 = make_uint2((x[0].x >> 16) | (x[1].x & 0xffff0000u),
-                                                (x[2].x >> 16) | (x[3].x & 0xffff0000u));
-                    const uint2 d2 = make_uint2((x[0].y & 0xffffu) | (x[1].y << 16),
-                                                (x[2].y & 0xffffu) | (x[3].y << 16));
-                    const uint2 d3 = make_uint2((x[0].y >> 16) | (x[1].y & 0xffff0000u),
-                                                (x[2].y >> 16) | (x[3].y & 0xffff0000u));
-                    uint16_t *base = &s_v[buf][(4 * dg) * C::VLD + 4 * kg];
-                    *reinterpret_cast<uint2 *>(base) = d0;
-                    *reinterpret_cast<uint2 *>(base + C::VLD) = d1;
-                    *reinterpret_cast<uint2 *>(base + 2 * C::VLD) = d2;
-                    *reinterpret_cast<uint2 *>(base + 3 * C::VLD) = d3;
-                }
-            }
+        // direct loads of tile kt into buffer buf (see load_kv_tile)
+        auto load_tile = [&](int kt, int buf) {
+            load_kv_tile<C>(a, kt * kBN, kmax_wg, shift, bmask, win0, blk0, kv_row, kv_head, w, lane,
+                            s_blk, s_k[buf], s_v[buf]);
         };
 
         stage_ids(0);
         __syncthreads();
-        load_tile(0);
-        store_tile(0);
+        blk0 = s_blk[0];
+        load_tile(0, 0);
+        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
 
-        const int pn = swap_bits_2_3(n);
         for (int j = 0; j < ntiles; ++j) {
             const int buf = j & 1;
             if (j + 1 < ntiles) {
@@ -270,25 +253,33 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_mfma_kernel(PfArgs a) {
                     stage_ids(kb1 >> shift);
                     __syncthreads();
                 }
-                load_tile(j + 1);
+                load_tile(j + 1, buf ^ 1);
             }
             const int kb = j * kBN;
             if (wave_active && kb <= kmax_w) {
-                // ---- S^T = K . Q^T for the 64 keys of this tile (two 32-key blocks)
+                const unsigned char *kt = s_k[buf];
+                const unsigned char *vt = s_v[buf];
+                // ---- S^T = K . Q^T: the A operands of each 32-key block from LDS in one batch
                 f32x16 sacc[2];
 #pragma unroll
                 for (int t = 0; t < 2; ++t)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) sacc[t][r] = 0.f;
 #pragma unroll
-                for (int ks = 0; ks < C::KS; ++ks) {
+                for (int t = 0; t < 2; ++t) {
+                    const int r = 32 * t + pn;
+                    bf16x8 ka[C::KS];
 #pragma unroll
-                    for (int t = 0; t < 2; ++t) {
-                        const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(
-                            &s_k[buf][(32 * t + pn) * C::KLD + 16 * ks + 8 * hf]);
-                        sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], sacc[t], 0, 0, 0);
-                    }
+                    for (int ks = 0; ks < C::KS; ++ks)
+                        ka[ks] = *reinterpret_cast<const bf16x8 *>(
+                            kt + r * C::ROWB + k_slot<C::CPR>(r, 2 * ks + hf) * 16);
+#pragma unroll
+                    for (int ks = 0; ks < C::KS; ++ks)
+                        sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qf[ks], sacc[t], 0, 0, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, C::KS, 0);  // LDS reads of the block
+                    __builtin_amdgcn_sched_group_barrier(0x008, C::KS, 0);  // then its MFMAs
                 }
+
                 // ---- mask (only tiles that cross the diagonal or the key end)
                 // register r of block t holds key kb + 32t + 16(r/8) + 8hf + r%8
                 if (kb + kBN - 1 > kfull_w) {
@@ -300,49 +291,69 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_mfma_kernel(PfArgs a) {
                             if (key > lim_me) sacc[t][r] = -INFINITY;
                         }
                 }
-                // ---- online softmax (log2 domain; scores scaled inside exp2)
+                // ---- online softmax (log2 domain; scores scaled inside exp2).
+                // The reference max m moves only when some lane's tile max exceeds
+                // it by more than kRescaleLog2 (wave-uniform decision); otherwise
+                // probabilities stay <= 2^kRescaleLog2 and O, l keep their scale.
+                // O / l is exact either way because both use the same m.
                 float mx = -INFINITY;
 #pragma unroll
                 for (int t = 0; t < 2; ++t)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[t][r]);
                 mx = fmaxf(mx, __shfl_xor(mx, 32));
-                const float m_new = fmaxf(m, mx);
-                const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-                const float alpha = exp2f((m - m_use) * c);
-                const float mc = m_use * c;
+                if (__any(mx * c > m * c + kRescaleLog2)) {
+                    const float m_new = fmaxf(m, mx);
+                    const float alpha = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m - m_new) * c);
+                    m = m_new;
+                    l *= alpha;
+#pragma unroll
+                    for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+                }
+                const float mc = (m == -INFINITY) ? 0.f : m * c;
                 float rs = 0.f;
                 bf16x8 pb[4];
 #pragma unroll
                 for (int st = 0; st < 4; ++st) {
-                    uint32_t w4[4];
+                    f32x8 pf;
 #pragma unroll
-                    for (int jj = 0; jj < 4; ++jj) {
-                        const float p0 = exp2f(fmaf(sacc[st >> 1][8 * (st & 1) + 2 * jj], c, -mc));
-                        const float p1 = exp2f(fmaf(sacc[st >> 1][8 * (st & 1) + 2 * jj + 1], c, -mc));
-                        rs += p0 + p1;
-                        w4[jj] = pack_bf16x2(p0, p1);
+                    for (int jj = 0; jj < 8; ++jj) {
+                        pf[jj] = __builtin_amdgcn_exp2f(fmaf(sacc[st >> 1][8 * (st & 1) + jj], c, -mc));
+                        rs += pf[jj];
                     }
-                    pb[st] = __builtin_bit_cast(bf16x8, make_uint4(w4[0], w4[1], w4[2], w4[3]));
+                    pb[st] = __builtin_convertvector(pf, bf16x8);
                 }
-                l = l * alpha + rs;
-                m = m_new;
+                l += rs;
+
+                // ---- O^T += V^T . P^T; V^T operands by LDS transpose loads:
+                // lane (group grp = lane/16, i = lane%16) names row 16st + 8hf + 4x + i/4
+                // (x = 0, 1) at column 32dt + 16(grp&1) + 4(i&3) and receives
+                // V[16st + 8hf + 4x + 0..3][32dt + lane%32].
+                const int grp = lane >> 4, li = lane & 15;
 #pragma unroll
-                for (int dt = 0; dt < C::DT; ++dt)
+                for (int st = 0; st < 4; ++st) {
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
-                // ---- O^T += V^T . P^T
+                    for (int dt = 0; dt < C::DT; ++dt) {
+                        i16x4 part[2];
 #pragma unroll
-                for (int dt = 0; dt < C::DT; ++dt) {
-#pragma unroll
-                    for (int st = 0; st < 4; ++st) {
-                        const bf16x8 va = *reinterpret_cast<const bf16x8 *>(
-                            &s_v[buf][(32 * dt + n) * C::VLD + 16 * st + 8 * hf]);
+                        for (int x = 0; x < 2; ++x) {
+                            const int r = 16 * st + 8 * hf + 4 * x + (li >> 2);
+                            const int col = 32 * dt + 16 * (grp & 1) + 4 * (li & 3);
+                            const unsigned char *addr = vt + r * C::ROWB +
+                                                        v_slot<C::CPR>(r, col >> 3) * 16 + (col & 7) * 2;
+                            part[x] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                (lds_i16x4 *)(addr));
+                        }
+                        const bf16x8 va = __builtin_bit_cast(
+                            bf16x8, (i16x8){part[0][0], part[0][1], part[0][2], part[0][3],
+                                            part[1][0], part[1][1], part[1][2], part[1][3]});
                         o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[st], o[dt], 0, 0, 0);
                     }
                 }
             }
-            if (j + 1 < ntiles) store_tile(buf ^ 1);
+            __builtin_amdgcn_s_waitcnt(0);  // this wave's direct loads of tile j+1 have landed
             __syncthreads();
         }
 
@@ -354,9 +365,10 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_mfma_kernel(PfArgs a) {
             for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
                 for (int b = 0; b < 4; ++b) {
-                    const uint2 v = make_uint2(pack_bf16x2(o[dt][4 * b] * inv, o[dt][4 * b + 1] * inv),
-                                               pack_bf16x2(o[dt][4 * b + 2] * inv, o[dt][4 * b + 3] * inv));
-                    *reinterpret_cast<uint2 *>(orow + 32 * dt + 8 * b + 4 * hf) = v;
+                    f32x4 v;
+#pragma unroll
+                    for (int a4 = 0; a4 < 4; ++a4) v[a4] = o[dt][4 * b + a4] * inv;
+                    *reinterpret_cast<bf16x4 *>(orow + 32 * dt + 8 * b + 4 * hf) = __builtin_convertvector(v, bf16x4);
                 }
         }
     }
