@@ -29,6 +29,9 @@ COMMON = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
     # no packed fp32 (v_pk_*_f32) instructions in generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in ordinary VGPRs: the prefill's O and S tiles then stay
+    # where the softmax and the rescale use them, with no AGPR copies
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-I", INCLUDE, "-I", CSRC, "-Wall",
 ]
 

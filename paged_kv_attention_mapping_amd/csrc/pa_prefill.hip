@@ -101,10 +101,12 @@ __device__ __forceinline__ int swap_bits_2_3(int i) {
     return (i & ~0xC) | ((i & 4) << 1) | ((i & 8) >> 1);
 }
 
-// 16-byte slot of logical chunk c in LDS row r: K rows use r, V rows use 2r
-// (the transpose reads touch 4 consecutive rows x 2 adjacent chunks).
+// 16-byte slot of logical chunk c in LDS row r.  K rows XOR with r: the 16
+// lanes of a K read name 16 different rows at one chunk.  V rows XOR with 4r:
+// a transpose read of 32 lanes names 4 consecutive rows x 4 adjacent chunks,
+// which 4r spreads over 16 different slots (all 64 banks).
 template <int CPR> __device__ __forceinline__ int k_slot(int r, int c) { return c ^ (r & (CPR - 1)); }
-template <int CPR> __device__ __forceinline__ int v_slot(int r, int c) { return c ^ ((2 * r) & (CPR - 1)); }
+template <int CPR> __device__ __forceinline__ int v_slot(int r, int c) { return c ^ ((4 * r) & (CPR - 1)); }
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
@@ -175,6 +177,19 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_mfma_kernel(PfArgs a) {
     const int64_t kv_row = (int64_t)a.hkv * D;      // elements per pool slot
     const int64_t kv_head = (int64_t)g * D;
     const int pn = swap_bits_2_3(n);
+    // byte offsets of this lane's V^T transpose reads within a tile, one per
+    // 32-wide d block: row 8hf + i/4, chunk (4dt + 2(grp&1) + (i&3)/2) ^ 4(i/4),
+    // byte 8(i&1) inside the chunk (i = lane%16, grp = lane/16)
+    int vrd[C::DT];
+    {
+        const int li = lane & 15, grp = lane >> 4;
+        const int row = 8 * hf + (li >> 2);
+#pragma unroll
+        for (int dt = 0; dt < C::DT; ++dt) {
+            const int chunk = 4 * dt + 2 * (grp & 1) + ((li & 3) >> 1);
+            vrd[dt] = row * C::ROWB + v_slot<C::CPR>(row, chunk) * 16 + 8 * (li & 1);
+        }
+    }
 
     for (int it = 0; it < 2; ++it) {
         const int tile = it == 0 ? T - 1 - pair : pair;
@@ -302,7 +317,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_mfma_kernel(PfArgs a) {
 #pragma unroll
                     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[t][r]);
                 mx = fmaxf(mx, __shfl_xor(mx, 32));
-                if (__any(mx * c > m * c + kRescaleLog2)) {
+                if (__builtin_expect(__any(mx * c > m * c + kRescaleLog2), 0)) {
                     const float m_new = fmaxf(m, mx);
                     const float alpha = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m - m_new) * c);
                     m = m_new;
@@ -330,22 +345,17 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_mfma_kernel(PfArgs a) {
                 // ---- O^T += V^T . P^T; V^T operands by LDS transpose loads:
                 // lane (group grp = lane/16, i = lane%16) names row 16st + 8hf + 4x + i/4
                 // (x = 0, 1) at column 32dt + 16(grp&1) + 4(i&3) and receives
-                // V[16st + 8hf + 4x + 0..3][32dt + lane%32].
-                const int grp = lane >> 4, li = lane & 15;
+                // V[16st + 8hf + 4x + 0..3][32dt + lane%32].  With the 4r swizzle the
+                // address is a per-lane base (one per dt) plus a constant per (st, x).
 #pragma unroll
                 for (int st = 0; st < 4; ++st) {
 #pragma unroll
                     for (int dt = 0; dt < C::DT; ++dt) {
                         i16x4 part[2];
 #pragma unroll
-                        for (int x = 0; x < 2; ++x) {
-                            const int r = 16 * st + 8 * hf + 4 * x + (li >> 2);
-                            const int col = 32 * dt + 16 * (grp & 1) + 4 * (li & 3);
-                            const unsigned char *addr = vt + r * C::ROWB +
-                                                        v_slot<C::CPR>(r, col >> 3) * 16 + (col & 7) * 2;
+                        for (int x = 0; x < 2; ++x)
                             part[x] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                                (lds_i16x4 *)(addr));
-                        }
+                                (lds_i16x4 *)(vt + vrd[dt] + (16 * st + 4 * x) * C::ROWB));
                         const bf16x8 va = __builtin_bit_cast(
                             bf16x8, (i16x8){part[0][0], part[0][1], part[0][2], part[0][3],
                                             part[1][0], part[1][1], part[1][2], part[1][3]});
