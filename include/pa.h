@@ -118,7 +118,8 @@ pa_status pa_store_kv(const void *k, int64_t k_row_stride,
  *                 row are read.
  *   max_seqlen_q, max_seqlen_k  host upper bounds of q_len(s) and k_len(s)
  *                 (they size the launch; no device read is needed).
- *   softmax_scale multiplies q . k before the softmax (usually 1/sqrt(d)).
+ *   softmax_scale multiplies q . k before the softmax (usually 1/sqrt(d));
+ *                 it must be finite and > 0 (else PA_ERR_BAD_SHAPE).
  *   out           [total_q][num_q_heads][head_dim] contiguous, `pool->dtype`
  *                 (bf16 output is rounded to nearest-even).
  *   workspace     device scratch of at least pa_prefill_workspace_bytes(...)
@@ -145,6 +146,7 @@ pa_status pa_prefill_varlen(const void *q, int64_t q_row_stride, int32_t num_q_h
  *                 0 .. context_lens[s]-1.  0 marks a padding row (output 0).
  *   block_table   int32 [num_seqs][block_table_stride].
  *   max_context_len  host upper bound of context_lens (sizes the launch).
+ *   softmax_scale as for pa_prefill_varlen (finite, > 0).
  *   out           [num_seqs][num_q_heads][head_dim] contiguous.
  *   workspace     >= pa_decode_workspace_bytes(...) bytes: split-K partial
  *                 results (running max, normaliser and fp32 accumulator per

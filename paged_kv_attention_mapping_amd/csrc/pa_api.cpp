@@ -55,6 +55,10 @@ pa_status check_attention_shape(const pa_pool *pool, int32_t num_q_heads, pa::Po
 
 pa_status from_hip(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
 
+// The kernels track a running max of the raw scores, which orders the scaled
+// scores the same way only for a positive scale.
+bool scale_ok(float s) { return s > 0.f && s <= 3.0e38f; }
+
 void say(char *why, size_t why_len, const char *fmt, long long a, long long b) {
     if (why && why_len) snprintf(why, why_len, fmt, a, b);
 }
@@ -127,6 +131,7 @@ pa_status pa_prefill_varlen(const void *q, int64_t q_row_stride, int32_t num_q_h
     pa_status st = check_attention_shape(pool, num_q_heads, &g);
     if (st != PA_OK) return st;
     if (num_seqs < 0 || total_q < 0 || max_seqlen_q < 0 || max_seqlen_k < 0) return PA_ERR_BAD_SHAPE;
+    if (!scale_ok(softmax_scale)) return PA_ERR_BAD_SHAPE;
     if (num_seqs == 0 || total_q == 0) return PA_OK;
     if (!q || !k_pool || !v_pool || !cu_seqlens_q || !cu_seqlens_k || !q_offsets || !block_table || !out)
         return PA_ERR_NULL_ARG;
@@ -161,6 +166,7 @@ pa_status pa_decode(const void *q, int64_t q_row_stride, int32_t num_q_heads, co
     pa_status st = check_attention_shape(pool, num_q_heads, &g);
     if (st != PA_OK) return st;
     if (num_seqs < 0 || max_context_len < 0) return PA_ERR_BAD_SHAPE;
+    if (!scale_ok(softmax_scale)) return PA_ERR_BAD_SHAPE;
     if (num_seqs == 0) return PA_OK;
     if (!q || !k_pool || !v_pool || !context_lens || !block_table || !out) return PA_ERR_NULL_ARG;
     if (block_table_stride <= 0) return PA_ERR_BAD_SHAPE;

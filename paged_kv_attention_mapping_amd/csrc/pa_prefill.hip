@@ -15,32 +15,41 @@
 // in-tile masks.
 //
 // Mapping on gfx950 (wave64, v_mfma_f32_32x32x16_bf16):
-//  * a wave owns 32 query positions of ONE query head; a workgroup of four
-//    waves owns NH query heads that share one KV head (GQA) times 4/NH
-//    position sub-tiles, so one K/V tile in LDS serves all of them.
+//  * a wave owns 32 query positions of ONE query head; four (head, position
+//    sub-tile) slots cover NH query heads that share one KV head (GQA) times
+//    4/NH sub-tiles, so one K/V tile in LDS serves all of them.
+//  * a workgroup has eight waves, two per SIMD: each slot is held by two
+//    waves that split the keys.  A step stages 128 keys; the first key half
+//    takes keys 0..63 of it, the second keys 64..127.  At the end the second
+//    half hands its (O, m, l) to the first through LDS, which merges them.
 //  * scores are computed transposed, S^T = K . Q^T (A = K rows from LDS,
 //    B = the wave's Q held in registers all along), so each lane owns one
-//    query's column: row max / sum need one exchange between the two lane
-//    halves only.
+//    query's column: sums need one exchange between the two lane halves.
 //  * K rows are fed to the MFMA in an order that swaps bits 2 and 3 of the
 //    row index inside each 32-row block.  With the 32x32 accumulator layout
 //    (lane half h, register r -> row 8*(r/4) + 4h + r%4) this puts the scores
 //    of keys 16s + 8h + (0..7) in registers 8s..8s+7 of lane half h, which is
 //    exactly the B operand layout of O^T = V^T . P^T: P never leaves registers.
-//  * K and V tiles go from HBM/L2 straight into LDS (16-byte direct loads, no
+//  * K and V rows go from HBM/L2 straight into LDS (16-byte direct loads, no
 //    staging registers), row-major with a 16-byte XOR swizzle per row, so both
 //    the K reads (ds_read_b128) and the V^T reads are free of bank conflicts.
+//    Each wave loads 16 rows of a step; when they are 16 visible keys of one
+//    valid block, a buffer resource over them (scalar registers) and fixed
+//    per-lane offsets make the loads free of per-lane address arithmetic.
 //  * the A operand of the PV product, V^T, is read with the gfx950 LDS
 //    transpose load ds_read_b64_tr_b16: in each 16-lane group, lane i gets
 //    element i%4 of the 8-byte chunks named by lanes 4r + i/4 (r = 0..3), so
 //    if lane 4r+q names V[key_r][d0 + 4q] it receives V[key_0..3][d0 + i].
+//  * softmax runs against a running reference max that moves only when a
+//    block's probabilities would grow too large (see attend_tile), so the hot
+//    path computes no per-tile max.
 //  * a workgroup processes a PAIR of query tiles of one sequence, tile p and
 //    tile T-1-p, so every workgroup of a sequence does the same causal work.
 //  * the KV head index varies fastest across workgroups; with 8 KV heads and
 //    workgroups dealt round-robin to the 8 XCDs, all tiles of one KV head run
 //    on one XCD and re-read its K/V from that XCD's L2.
-//  * K/V tiles are double-buffered in LDS: the direct loads of tile j+1 are in
-//    flight while tile j is computed.  Block ids are staged in LDS per window.
+//  * steps are double-buffered in LDS: the direct loads of step j+1 are in
+//    flight while step j is computed.  Block ids are staged in LDS per window.
 //  * rows a tile holds past the last needed key are loaded from the sequence's
 //    key 0 (finite data), so masked probabilities (exact zeros) never meet
 //    uninitialised pool contents (0 * NaN).
@@ -58,23 +67,30 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kPfThreads = 256;
-constexpr int kBN = 64;       // keys per tile
-constexpr int kBlkWin = 1024;  // block ids staged in LDS at a time
+constexpr int kPfWaves = 8;                   // two waves per SIMD
+constexpr int kPfThreads = 64 * kPfWaves;
+constexpr int kBN = 64;                       // keys per wave tile
+constexpr int kStep = 2 * kBN;                // keys per workgroup step: one tile per key half
+constexpr int kRowsPerWave = kStep / kPfWaves;  // step rows each wave loads (16)
+constexpr int kBlkWin = 1024;                 // block ids staged in LDS at a time
 constexpr float kLog2eF = 1.4426950408889634f;
-constexpr float kRescaleLog2 = 8.f;  // lazy-rescale threshold (log2 units)
 
 template <int D, int NH>
 struct Pf {
-    static constexpr int SUB = 4 / NH;                     // position sub-tiles per workgroup
-    static constexpr int BM = 32 * SUB;                    // positions per workgroup tile
-    static constexpr int KS = D / 16;                      // MFMA k-steps over head_dim
-    static constexpr int DT = D / 32;                      // 32-wide output tiles over head_dim
-    static constexpr int CPR = D / 8;                      // 16-byte chunks per row
-    static constexpr int ROWB = D * 2;                     // bytes per LDS row (bf16)
-    static constexpr int TILEB = kBN * ROWB;               // bytes per K or V tile
-    static constexpr int LPW = TILEB / (kPfThreads * 16);  // direct 16-byte loads per lane per tile
-    static_assert(LPW >= 1 && TILEB % (kPfThreads * 16) == 0, "tile split");
+    static constexpr int SUB = 4 / NH;                 // position sub-tiles per workgroup
+    static constexpr int BM = 32 * SUB;                // positions per workgroup tile
+    static constexpr int KS = D / 16;                  // MFMA k-steps over head_dim
+    static constexpr int DT = D / 32;                  // 32-wide output tiles over head_dim
+    static constexpr int CPR = D / 8;                  // 16-byte chunks per row
+    static constexpr int ROWB = D * 2;                 // bytes per LDS row (bf16)
+    static constexpr int TILEB = kBN * ROWB;           // bytes of one wave tile (K or V)
+    static constexpr int STEPB = kStep * ROWB;         // bytes of one step (K or V)
+    static constexpr int RPI = 64 / CPR;               // rows per wave-wide 16-byte load
+    static constexpr int LPW = kRowsPerWave / RPI;     // 16-byte loads per lane per step (K or V)
+    static constexpr int MERGE = DT * 16 + 2;          // floats per lane handed between key halves
+    static_assert(LPW * RPI == kRowsPerWave && LPW >= 1, "row split");
+    static_assert((4 * RPI) % CPR == 0, "V swizzle independent of the load index");
+    static_assert(4 * MERGE * 64 * 4 <= 4 * STEPB, "merge area fits in the K/V buffers");
 };
 
 struct PfArgs {
@@ -110,25 +126,77 @@ template <int CPR> __device__ __forceinline__ int v_slot(int r, int c) { return 
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-// Direct HBM/L2 -> LDS loads of one K tile and one V tile (kBN keys x D).
-// Slot q of a tile (16 bytes) is written by lane q%64 of wave-instruction q/64
-// and holds chunk (slot ^ swizzle) of row q / CPR.  Keys past kmax (masked for
-// every row; their blocks are not staged) and keys in blocks outside the pool
-// are read from key 0 of the sequence (blk0) instead: finite data that the
-// zero probabilities cancel.
+// Max / sum of x over lanes i and i^32 (the two 32-lane halves), in every
+// lane, with one v_permlane32_swap: it exchanges lanes 32..63 of its first
+// operand with lanes 0..31 of its second, so with x in both, one result holds
+// the lane's own x and the other its partner's.
+__device__ __forceinline__ float halves_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Buffer resource over `bytes` bytes from p: raw (stride 0) addressing with
+// 32-bit data format, the gfx9 default for untyped buffer loads.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void *p, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, bytes, 0x00020000);
+}
+
+// Direct HBM/L2 -> LDS loads of this wave's 16 rows of one step (keys
+// kb_step + 16w .. +15) into the step buffers dk / dv.  Slot q of the wave's
+// rows (16 bytes) is written by lane q%64 of its wave-instruction q/64 and
+// holds chunk (slot ^ swizzle) of row q / CPR.
+//  * fast path: when all 16 rows are visible keys of one valid block (block
+//    size >= 16), a buffer resource over the 16 pool rows (wave-uniform, in
+//    scalar registers) is read at per-lane 32-bit offsets (koff / voff: row
+//    lane/CPR of each RPI-row group, swizzled chunk of slot lane%CPR) plus a
+//    scalar offset of RPI rows per load;
+//  * otherwise each lane resolves its own row: keys past kmax (masked for
+//    every row; their blocks are not staged) and keys in blocks outside the
+//    pool are read from key 0 of the sequence (blk0) instead, finite data
+//    that the zero probabilities cancel;
+//  * rows of a wave tile that no wave computes are not loaded.
 template <class C>
-__device__ __forceinline__ void load_kv_tile(const PfArgs &a, int kb, int kmax, int shift, int bmask,
-                                             int win0, int blk0, int64_t kv_row, int64_t kv_head,
-                                             int w, int lane, const int *s_blk, unsigned char *dk,
-                                             unsigned char *dv) {
+__device__ __forceinline__ void load_wave_rows(const PfArgs &a, int kb_step, int kmax, int shift, int bmask,
+                                               int win0, int blk0, int64_t kv_row, int64_t kv_head,
+                                               const uint32_t (&koff)[C::LPW], uint32_t voff, int w, int lane,
+                                               const int *s_blk, unsigned char *dk, unsigned char *dv) {
+    if (kb_step + kBN * (w / (kPfWaves / 2)) > kmax) return;
+    const int row0 = __builtin_amdgcn_readfirstlane(kb_step + kRowsPerWave * w);
+    if (shift >= 4 && row0 + kRowsPerWave - 1 <= kmax) {
+        const int p = __builtin_amdgcn_readfirstlane(s_blk[(row0 >> shift) - win0]);
+        if (p >= 0) {
+            const int row_bytes = (int)(kv_row * 2);
+            const int64_t sbase = ((((int64_t)p << shift) + (row0 & bmask)) * kv_row + kv_head) * 2;
+            const __amdgpu_buffer_rsrc_t rk =
+                raw_rsrc(reinterpret_cast<const unsigned char *>(a.k_pool) + sbase, kRowsPerWave * row_bytes);
+            const __amdgpu_buffer_rsrc_t rv =
+                raw_rsrc(reinterpret_cast<const unsigned char *>(a.v_pool) + sbase, kRowsPerWave * row_bytes);
+#pragma unroll
+            for (int u = 0; u < C::LPW; ++u) {
+                const int dst = __builtin_amdgcn_readfirstlane((w * C::LPW + u) * 1024);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void *)(dk + dst), 16,
+                                                         koff[u], u * C::RPI * row_bytes, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void *)(dv + dst), 16, voff,
+                                                         u * C::RPI * row_bytes, 0, 0);
+            }
+            return;
+        }
+    }
 #pragma unroll
     for (int u = 0; u < C::LPW; ++u) {
-        const int blk_i = w * C::LPW + u;  // 1 KiB block of the tile
+        const int blk_i = w * C::LPW + u;  // 1 KiB block of the step
         const int q = blk_i * 64 + lane;
         const int r = q / C::CPR, sl = q % C::CPR;
-        const int key = kb + r;
+        const int key = kb_step + r;
         const int p = key <= kmax ? s_blk[(key >> shift) - win0] : -1;
         const int64_t slot = p >= 0 ? ((int64_t)p << shift) + (key & bmask)
                                     : (blk0 >= 0 ? ((int64_t)blk0 << shift) : 0);
@@ -140,15 +208,161 @@ __device__ __forceinline__ void load_kv_tile(const PfArgs &a, int kb, int kmax, 
     }
 }
 
+// Probabilities of one 32-key block of the tile (scores sacc), scaled by
+// the running reference max m: P = exp2(s*c - m*c), rounded to bf16 once so
+// that the PV product and the row sum (dot products with ones) see the same
+// weights.  Returns this lane's sum over its 16 keys of the block.
+template <class C>
+__device__ __forceinline__ float block_probs(const f32x16 &sacc, float c, float mc, bf16x8 &p_lo, bf16x8 &p_hi) {
+    const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
+    f32x8 lo, hi;
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+        lo[jj] = __builtin_amdgcn_exp2f(fmaf(sacc[jj], c, -mc));
+        hi[jj] = __builtin_amdgcn_exp2f(fmaf(sacc[8 + jj], c, -mc));
+    }
+    p_lo = __builtin_convertvector(lo, bf16x8);
+    p_hi = __builtin_convertvector(hi, bf16x8);
+    float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; k += 2) {
+        s0 = __builtin_amdgcn_fdot2_f32_bf16((bf16x2){p_lo[k], p_lo[k + 1]}, ones, s0, false);
+        s1 = __builtin_amdgcn_fdot2_f32_bf16((bf16x2){p_hi[k], p_hi[k + 1]}, ones, s1, false);
+    }
+    return s0 + s1;
+}
+
+// O^T += V^T . P^T for the 16-key group st of the tile; V^T operands by LDS
+// transpose loads: lane (group grp = lane/16, i = lane%16) names row 16st +
+// 8hf + 4x + i/4 (x = 0, 1) at column 32dt + 16(grp&1) + 4(i&3) and receives
+// V[16st + 8hf + 4x + 0..3][32dt + lane%32].  With the 4r swizzle the address
+// is a per-lane base (one per dt) plus a constant per (st, x).
+template <class C>
+__device__ __forceinline__ void pv_group(const unsigned char *vt, const int (&vrd)[C::DT], int st, const bf16x8 &pb,
+                                         f32x16 (&o)[C::DT]) {
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt) {
+        i16x4 part[2];
+#pragma unroll
+        for (int x = 0; x < 2; ++x)
+            part[x] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(vt + vrd[dt] + (16 * st + 4 * x) * C::ROWB));
+        const bf16x8 va = __builtin_bit_cast(bf16x8, (i16x8){part[0][0], part[0][1], part[0][2], part[0][3],
+                                                              part[1][0], part[1][1], part[1][2], part[1][3]});
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, o[dt], 0, 0, 0);
+    }
+}
+
+// Largest per-lane block sum of probabilities accepted without moving the
+// reference max: every P <= 2^20, so O and l stay far inside fp32 range.
+constexpr float kBlockSumMax = 1048576.f;
+
+// Cold path of one block: move the reference max to the block max (the same
+// in both lane halves of each query column), rescale O and l, and
+// exponentiate the block again.
+template <class C>
+__device__ __forceinline__ float rebase_block(const f32x16 &sacc, f32x16 (&o)[C::DT], float &m, float &l,
+                                             float c, bf16x8 &p_lo, bf16x8 &p_hi) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[r]);
+    mx = halves_max(mx);
+    const float m_new = fmaxf(m, mx);
+    const float alpha = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m - m_new) * c);
+    m = m_new;
+    l *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+    const float mc = (m == -INFINITY) ? 0.f : m * c;
+    return block_probs<C>(sacc, c, mc, p_lo, p_hi);
+}
+
+// Sets the scores of keys hidden from the lane's position to -inf in block
+// t: register r holds key kb + 32t + 16(r/8) + 8hf + r%8, hidden when
+// 32t + 16(r/8) + r%8 > thr.  The empty asm keeps the guarded call a real
+// branch (no selects on tiles that need no mask).
+__device__ __forceinline__ void mask_block(f32x16 &sacc, int t, int thr) {
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+        if (32 * t + 16 * (r >> 3) + (r & 7) > thr) sacc[r] = -INFINITY;
+}
+
+// One wave tile: 64 keys (rows of kt / vt in LDS) against the wave's 32
+// query positions, in two 32-key blocks.  need_mask: the tile crosses the
+// causal diagonal or the key end of some position (thr = last visible key -
+// kb - 8hf).
+//
+// Online softmax without a max per tile: each block is exponentiated against
+// the running reference max m (log2 domain, scores scaled inside exp2).
+// Only if some lane's block sum exceeds kBlockSumMax (or no m is set yet)
+// does the wave take the cold path (rebase_block).  O / l is exact
+// whatever m is, since both use it.  The hot path has no branch between
+// block 1's QK MFMAs and block 0's exponentials, nor between block 0's PV
+// MFMAs and block 1's exponentials, so the two can be issued interleaved.
+template <class C>
+__device__ __forceinline__ void attend_tile(const unsigned char *kt, const unsigned char *vt,
+                                            const bf16x8 (&qf)[C::KS], f32x16 (&o)[C::DT], float &m,
+                                            float &l, bool &m_set, bool need_mask, int thr, float c, int pn,
+                                            int hf, const int (&vrd)[C::DT]) {
+    // ---- S^T = K . Q^T per 32-key block t: A operands (K rows) from LDS
+    f32x16 sacc[2];
+    bf16x8 ka[2][C::KS];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[t][r] = 0.f;
+        const int r = 32 * t + pn;
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks)
+            ka[t][ks] = *reinterpret_cast<const bf16x8 *>(kt + r * C::ROWB + k_slot<C::CPR>(r, 2 * ks + hf) * 16);
+    }
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks)
+        sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[0][ks], qf[ks], sacc[0], 0, 0, 0);
+    if (need_mask) mask_block(sacc[0], 0, thr);
+
+    // ---- block 1's QK MFMAs; block 0's probabilities
+    float mc = (m == -INFINITY) ? 0.f : m * c;
+    bf16x8 p0_lo, p0_hi, p1_lo, p1_hi;
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks)
+        sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[1][ks], qf[ks], sacc[1], 0, 0, 0);
+    float ls = block_probs<C>(sacc[0], c, mc, p0_lo, p0_hi);
+    if (__builtin_expect(!m_set || __any(!(ls <= kBlockSumMax)), 0)) {
+        ls = rebase_block<C>(sacc[0], o, m, l, c, p0_lo, p0_hi);
+        m_set = true;
+        mc = (m == -INFINITY) ? 0.f : m * c;
+    }
+    l += ls;
+    if (need_mask) mask_block(sacc[1], 1, thr);
+
+    // ---- block 0's PV MFMAs; block 1's probabilities
+    pv_group<C>(vt, vrd, 0, p0_lo, o);
+    pv_group<C>(vt, vrd, 1, p0_hi, o);
+    ls = block_probs<C>(sacc[1], c, mc, p1_lo, p1_hi);
+    if (__builtin_expect(__any(!(ls <= kBlockSumMax)), 0)) ls = rebase_block<C>(sacc[1], o, m, l, c, p1_lo, p1_hi);
+    l += ls;
+
+    // ---- block 1's PV MFMAs
+    pv_group<C>(vt, vrd, 2, p1_lo, o);
+    pv_group<C>(vt, vrd, 3, p1_hi, o);
+}
+
 template <int D, int NH>
 __global__ __launch_bounds__(kPfThreads, 1) void prefill_mfma_kernel(PfArgs a) {
     using C = Pf<D, NH>;
-    __shared__ __attribute__((aligned(1024))) unsigned char s_k[2][C::TILEB];
-    __shared__ __attribute__((aligned(1024))) unsigned char s_v[2][C::TILEB];
+    // [buffer][K, V][step rows]; after the key loop the same memory carries
+    // the second key half's partial results to the first
+    __shared__ __attribute__((aligned(1024))) unsigned char s_kv[2][2][C::STEPB];
     __shared__ int s_blk[kBlkWin];
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = tid >> 6;
     const int n = lane & 31, hf = lane >> 5;
+    const int kh = w / (kPfWaves / 2);  // key half: tile kh of every step
+    const int wl = w % (kPfWaves / 2);  // (head, position sub-tile) slot
 
     int64_t wg = blockIdx.x;
     const int g = (int)(wg % a.hkv);
@@ -165,7 +379,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_mfma_kernel(PfArgs a) {
     const int T = (q_len + C::BM - 1) / C::BM;
     if (pair >= (T + 1) / 2) return;
 
-    const int hh = w % NH, sub = w / NH;
+    const int hh = wl % NH, sub = wl / NH;
     const int h = g * a.group + hgrp * NH + hh;
     const int hq = a.hkv * a.group;
     const int shift = a.block_shift;
@@ -174,7 +388,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_mfma_kernel(PfArgs a) {
     // keys that may be indexed: within k_len and within the table row
     const int kcap = (int)min((int64_t)k_len, (int64_t)a.bt_stride << shift);
     const float c = a.scale_log2;
-    const int64_t kv_row = (int64_t)a.hkv * D;      // elements per pool slot
+    const int64_t kv_row = (int64_t)a.hkv * D;  // elements per pool slot
     const int64_t kv_head = (int64_t)g * D;
     const int pn = swap_bits_2_3(n);
     // byte offsets of this lane's V^T transpose reads within a tile, one per
@@ -190,6 +404,18 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_mfma_kernel(PfArgs a) {
             vrd[dt] = row * C::ROWB + v_slot<C::CPR>(row, chunk) * 16 + 8 * (li & 1);
         }
     }
+    // byte offsets, inside the pool, of this lane's 16-byte pieces of the
+    // wave's 16 rows (fast load path): row RPI*u + lane/CPR of the wave,
+    // swizzled chunk of slot lane%CPR
+    // (the row RPI*u itself is a scalar offset; the V swizzle is the same for
+    // every u because 4*RPI is a multiple of CPR)
+    uint32_t koff[C::LPW];
+    const uint32_t voff = (uint32_t)((lane / C::CPR) * kv_row * 2 + v_slot<C::CPR>(lane / C::CPR, lane % C::CPR) * 16);
+#pragma unroll
+    for (int u = 0; u < C::LPW; ++u)
+        koff[u] = (uint32_t)((lane / C::CPR) * kv_row * 2 +
+                             k_slot<C::CPR>(C::RPI * u + lane / C::CPR, lane % C::CPR) * 16);
+    float *merge = reinterpret_cast<float *>(&s_kv[0][0][0]) + wl * (C::MERGE * 64);
 
     for (int it = 0; it < 2; ++it) {
         const int tile = it == 0 ? T - 1 - pair : pair;
@@ -208,11 +434,11 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_mfma_kernel(PfArgs a) {
         uint16_t *orow = a.out + ((int64_t)(q_start + i_me) * hq + h) * D;
 
         if (kmax_wg < 0) {  // no keys at all (k_len == 0): zero output
-            if (row_ok && hf == 0)
+            if (kh == 0 && row_ok && hf == 0)
                 for (int d = 0; d < D; ++d) orow[d] = 0;
             continue;
         }
-        const int ntiles = kmax_wg / kBN + 1;
+        const int nsteps = kmax_wg / kStep + 1;
         const int last_blk = kmax_wg >> shift;
 
         // the wave's queries, B operand layout: lane (n, hf), k-step ks holds d = 16ks + 8hf .. +7
@@ -231,6 +457,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_mfma_kernel(PfArgs a) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
         float m = -INFINITY, l = 0.f;
+        bool m_set = false;  // wave-uniform: some block has set the reference max
 
         // block-id window staging (every thread reads ids only after a barrier)
         int win0 = 0;
@@ -242,145 +469,72 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_mfma_kernel(PfArgs a) {
                 s_blk[i] = (p >= 0 && (int64_t)p < a.num_blocks) ? p : -1;
             }
         };
-        // Keys past kmax_wg (masked for every row; their blocks are not staged)
-        // and keys in blocks outside the pool are read from key 0 of the
-        // sequence instead: finite data that the zero probabilities cancel.
-        int blk0 = -1;  // physical block of key 0 (finite stand-in for masked rows)
-
-        // direct loads of tile kt into buffer buf (see load_kv_tile)
-        auto load_tile = [&](int kt, int buf) {
-            load_kv_tile<C>(a, kt * kBN, kmax_wg, shift, bmask, win0, blk0, kv_row, kv_head, w, lane,
-                            s_blk, s_k[buf], s_v[buf]);
-        };
-
         stage_ids(0);
         __syncthreads();
-        blk0 = s_blk[0];
-        load_tile(0, 0);
+        const int blk0 = s_blk[0];  // physical block of key 0 (finite stand-in for masked rows)
+        load_wave_rows<C>(a, 0, kmax_wg, shift, bmask, win0, blk0, kv_row, kv_head, koff, voff, w, lane, s_blk,
+                          s_kv[0][0], s_kv[0][1]);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
 
-        for (int j = 0; j < ntiles; ++j) {
+        for (int j = 0; j < nsteps; ++j) {
             const int buf = j & 1;
-            if (j + 1 < ntiles) {
-                const int kb1 = (j + 1) * kBN;
-                if (((kb1 + kBN - 1) >> shift) >= win0 + kBlkWin) {  // leave the staged window
+            if (j + 1 < nsteps) {
+                const int kb1 = (j + 1) * kStep;
+                if ((min(kb1 + kStep - 1, kmax_wg) >> shift) >= win0 + kBlkWin) {  // leave the staged window
                     stage_ids(kb1 >> shift);
                     __syncthreads();
                 }
-                load_tile(j + 1, buf ^ 1);
+                load_wave_rows<C>(a, kb1, kmax_wg, shift, bmask, win0, blk0, kv_row, kv_head, koff, voff, w,
+                                  lane, s_blk, s_kv[buf ^ 1][0], s_kv[buf ^ 1][1]);
             }
-            const int kb = j * kBN;
+            const int kb = j * kStep + kh * kBN;
             if (wave_active && kb <= kmax_w) {
-                const unsigned char *kt = s_k[buf];
-                const unsigned char *vt = s_v[buf];
-                // ---- S^T = K . Q^T: the A operands of each 32-key block from LDS in one batch
-                f32x16 sacc[2];
-#pragma unroll
-                for (int t = 0; t < 2; ++t)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) sacc[t][r] = 0.f;
-#pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    const int r = 32 * t + pn;
-                    bf16x8 ka[C::KS];
-#pragma unroll
-                    for (int ks = 0; ks < C::KS; ++ks)
-                        ka[ks] = *reinterpret_cast<const bf16x8 *>(
-                            kt + r * C::ROWB + k_slot<C::CPR>(r, 2 * ks + hf) * 16);
-#pragma unroll
-                    for (int ks = 0; ks < C::KS; ++ks)
-                        sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qf[ks], sacc[t], 0, 0, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x100, C::KS, 0);  // LDS reads of the block
-                    __builtin_amdgcn_sched_group_barrier(0x008, C::KS, 0);  // then its MFMAs
-                }
-
-                // ---- mask (only tiles that cross the diagonal or the key end)
-                // register r of block t holds key kb + 32t + 16(r/8) + 8hf + r%8
-                if (kb + kBN - 1 > kfull_w) {
-#pragma unroll
-                    for (int t = 0; t < 2; ++t)
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            const int key = kb + 32 * t + 16 * (r >> 3) + 8 * hf + (r & 7);
-                            if (key > lim_me) sacc[t][r] = -INFINITY;
-                        }
-                }
-                // ---- online softmax (log2 domain; scores scaled inside exp2).
-                // The reference max m moves only when some lane's tile max exceeds
-                // it by more than kRescaleLog2 (wave-uniform decision); otherwise
-                // probabilities stay <= 2^kRescaleLog2 and O, l keep their scale.
-                // O / l is exact either way because both use the same m.
-                float mx = -INFINITY;
-#pragma unroll
-                for (int t = 0; t < 2; ++t)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[t][r]);
-                mx = fmaxf(mx, __shfl_xor(mx, 32));
-                if (__builtin_expect(__any(mx * c > m * c + kRescaleLog2), 0)) {
-                    const float m_new = fmaxf(m, mx);
-                    const float alpha = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m - m_new) * c);
-                    m = m_new;
-                    l *= alpha;
-#pragma unroll
-                    for (int dt = 0; dt < C::DT; ++dt)
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
-                }
-                const float mc = (m == -INFINITY) ? 0.f : m * c;
-                float rs = 0.f;
-                bf16x8 pb[4];
-#pragma unroll
-                for (int st = 0; st < 4; ++st) {
-                    f32x8 pf;
-#pragma unroll
-                    for (int jj = 0; jj < 8; ++jj) {
-                        pf[jj] = __builtin_amdgcn_exp2f(fmaf(sacc[st >> 1][8 * (st & 1) + jj], c, -mc));
-                        rs += pf[jj];
-                    }
-                    pb[st] = __builtin_convertvector(pf, bf16x8);
-                }
-                l += rs;
-
-                // ---- O^T += V^T . P^T; V^T operands by LDS transpose loads:
-                // lane (group grp = lane/16, i = lane%16) names row 16st + 8hf + 4x + i/4
-                // (x = 0, 1) at column 32dt + 16(grp&1) + 4(i&3) and receives
-                // V[16st + 8hf + 4x + 0..3][32dt + lane%32].  With the 4r swizzle the
-                // address is a per-lane base (one per dt) plus a constant per (st, x).
-#pragma unroll
-                for (int st = 0; st < 4; ++st) {
-#pragma unroll
-                    for (int dt = 0; dt < C::DT; ++dt) {
-                        i16x4 part[2];
-#pragma unroll
-                        for (int x = 0; x < 2; ++x)
-                            part[x] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                                (lds_i16x4 *)(vt + vrd[dt] + (16 * st + 4 * x) * C::ROWB));
-                        const bf16x8 va = __builtin_bit_cast(
-                            bf16x8, (i16x8){part[0][0], part[0][1], part[0][2], part[0][3],
-                                            part[1][0], part[1][1], part[1][2], part[1][3]});
-                        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[st], o[dt], 0, 0, 0);
-                    }
-                }
+                const unsigned char *kt = s_kv[buf][0] + kh * C::TILEB;
+                const unsigned char *vt = s_kv[buf][1] + kh * C::TILEB;
+                const int thr = lim_me - kb - 8 * hf;
+                attend_tile<C>(kt, vt, qf, o, m, l, m_set, kb + kBN - 1 > kfull_w, thr, c, pn, hf, vrd);
             }
-            __builtin_amdgcn_s_waitcnt(0);  // this wave's direct loads of tile j+1 have landed
+            __builtin_amdgcn_s_waitcnt(0);  // this wave's direct loads of step j+1 have landed
             __syncthreads();
         }
 
-        // ---- epilogue: O = O^T / l; lane (n, hf) holds d = 32dt + 8b + 4hf + a at register a + 4b
-        const float l_tot = l + __shfl_xor(l, 32);
-        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-        if (row_ok) {
+        // ---- the second key half hands (O, m, l) to the first through LDS
+        if (kh == 1) {
 #pragma unroll
             for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    f32x4 v;
-#pragma unroll
-                    for (int a4 = 0; a4 < 4; ++a4) v[a4] = o[dt][4 * b + a4] * inv;
-                    *reinterpret_cast<bf16x4 *>(orow + 32 * dt + 8 * b + 4 * hf) = __builtin_convertvector(v, bf16x4);
-                }
+                for (int r = 0; r < 16; ++r) merge[(dt * 16 + r) * 64 + lane] = o[dt][r];
+            merge[(C::DT * 16) * 64 + lane] = m;
+            merge[(C::DT * 16 + 1) * 64 + lane] = l;
         }
+        __syncthreads();
+        if (kh == 0) {
+            const float m2 = merge[(C::DT * 16) * 64 + lane];
+            const float l2 = merge[(C::DT * 16 + 1) * 64 + lane];
+            const float mn = fmaxf(m, m2);
+            const float a1 = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m - mn) * c);
+            const float a2 = (m2 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m2 - mn) * c);
+            l = l * a1 + l2 * a2;
+            // ---- epilogue: O = O^T / l; lane (n, hf) holds d = 32dt + 8b + 4hf + a at register a + 4b
+            const float l_tot = halves_sum(l);
+            const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+            if (row_ok) {
+#pragma unroll
+                for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+                    for (int b = 0; b < 4; ++b) {
+                        f32x4 v;
+#pragma unroll
+                        for (int a4 = 0; a4 < 4; ++a4) {
+                            const int r = 4 * b + a4;
+                            v[a4] = (o[dt][r] * a1 + merge[(dt * 16 + r) * 64 + lane] * a2) * inv;
+                        }
+                        *reinterpret_cast<bf16x4 *>(orow + 32 * dt + 8 * b + 4 * hf) = __builtin_convertvector(v, bf16x4);
+                    }
+            }
+        }
+        __syncthreads();  // the merge area is the next tile's K/V buffer
     }
 }
 
@@ -411,8 +565,11 @@ hipError_t dispatch_nh(const PfArgs &a, int num_seqs, int max_seqlen_q, hipStrea
 }  // namespace
 
 bool prefill_mfma_supported(const PoolGeom &g, int group) {
+    // 16 pool rows (one wave's share of a step) must span < 2^31 bytes for
+    // the 32-bit buffer offsets
     return g.dtype == 1 && (g.d == 64 || g.d == 128) && g.block_size >= 4 &&
-           (group == 1 || group == 2 || group == 4 || group == 8);
+           (group == 1 || group == 2 || group == 4 || group == 8) &&
+           (int64_t)g.hkv * g.d * 2 * kRowsPerWave < ((int64_t)1 << 31);
 }
 
 hipError_t launch_prefill_mfma(const void *q, int64_t q_row_stride, int hq, const void *k_pool,

@@ -65,6 +65,13 @@ def test_host_argument_errors_return_before_launch():
                          None, None, 0, None) == 0
     assert lib.pa_decode(None, 64, 4, None, None, ctypes.byref(pool), None, None, 1, 3, 10, 0.1,
                          None, None, 0, None) == 1
+    # the softmax scale must be finite and positive (checked before any pointer)
+    for scale in (0.0, -0.1, float("inf"), float("nan")):
+        assert lib.pa_decode(None, 64, 4, None, None, ctypes.byref(pool), None, None, 1, 3, 10, scale,
+                             None, None, 0, None) == 2
+        args = [None, 64, 4, None, None, ctypes.byref(pool), None, None, None, None, 1, 1, 1, 1, 1, scale,
+                None, None, 0, None]
+        assert lib.pa_prefill_varlen(*args) == 2
 
 
 def test_workspace_sizes_follow_the_split_plan():
