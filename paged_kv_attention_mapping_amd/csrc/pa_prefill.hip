@@ -55,6 +55,8 @@
 //    uninitialised pool contents (0 * NaN).
 #include <math.h>
 
+#include <type_traits>
+
 #include "pa_device.h"
 #include "pa_kernels.h"
 
@@ -301,60 +303,139 @@ __device__ __forceinline__ void mask_block(f32x16 &sacc, int t, int thr) {
 // whatever m is, since both use it.  The hot path has no branch between
 // block 1's QK MFMAs and block 0's exponentials, nor between block 0's PV
 // MFMAs and block 1's exponentials, so the two can be issued interleaved.
+// V^T operand of the PV MFMA for 16-key group st and d block dt: two LDS
+// transpose reads at the lane's base vofs[dt] plus an immediate offset (see
+// the kernel for the lane mapping).
 template <class C>
-__device__ __forceinline__ void attend_tile(const unsigned char *kt, const unsigned char *vt,
-                                            const bf16x8 (&qf)[C::KS], f32x16 (&o)[C::DT], float &m,
-                                            float &l, bool &m_set, bool need_mask, int thr, float c, int pn,
-                                            int hf, const int (&vrd)[C::DT]) {
-    // ---- S^T = K . Q^T per 32-key block t: A operands (K rows) from LDS
+__device__ __forceinline__ bf16x8 read_vt(const unsigned char *vbuf, const int (&vofs)[C::DT], int st, int dt) {
+    i16x4 part[2];
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+        part[x] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4 *)(vbuf + vofs[dt] + (16 * st + 4 * x) * C::ROWB));
+    return __builtin_bit_cast(bf16x8, (i16x8){part[0][0], part[0][1], part[0][2], part[0][3], part[1][0],
+                                             part[1][1], part[1][2], part[1][3]});
+}
+
+// Probabilities of scores 2i, 2i+1 of a block's 16 against the scaled
+// reference max mc (one slice of block_probs).
+__device__ __forceinline__ void probs_step(const f32x16 &sacc, float c, float mc, int i, f32x16 &pf) {
+    pf[2 * i] = __builtin_amdgcn_exp2f(fmaf(sacc[2 * i], c, -mc));
+    pf[2 * i + 1] = __builtin_amdgcn_exp2f(fmaf(sacc[2 * i + 1], c, -mc));
+}
+
+// bf16 probabilities and the lane's sum of them (see block_probs).
+__device__ __forceinline__ float probs_finish(const f32x16 &pf, bf16x8 &p_lo, bf16x8 &p_hi) {
+    const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
+    p_lo = __builtin_convertvector(__builtin_shufflevector(pf, pf, 0, 1, 2, 3, 4, 5, 6, 7), bf16x8);
+    p_hi = __builtin_convertvector(__builtin_shufflevector(pf, pf, 8, 9, 10, 11, 12, 13, 14, 15), bf16x8);
+    float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; k += 2) {
+        s0 = __builtin_amdgcn_fdot2_f32_bf16((bf16x2){p_lo[k], p_lo[k + 1]}, ones, s0, false);
+        s1 = __builtin_amdgcn_fdot2_f32_bf16((bf16x2){p_hi[k], p_hi[k + 1]}, ones, s1, false);
+    }
+    return s0 + s1;
+}
+
+// Running softmax state of one wave: reference max m (raw score units), mc =
+// m * c (0 while m is -inf), O^T accumulators, row-sum l, and whether any
+// block has set m yet (wave-uniform).
+template <class C>
+struct SoftState {
+    f32x16 o[C::DT];
+    float m, mc, l;
+    bool m_set;
+};
+
+// One wave tile: 64 keys against the wave's 32 query positions, in two
+// 32-key blocks.  kbuf / vbuf: bases of the step buffer (compile-time
+// offsets); kofs / vofs: the lane's byte offsets of its K rows and V^T pieces
+// from them (key half included).  need_mask: the tile crosses the causal diagonal
+// or the key end of some position (thr = last visible key - kb - 8hf).
+//
+// Online softmax without a max per tile: each block is exponentiated against
+// the running reference max (log2 domain, scores scaled inside exp2).  Only
+// if some lane's block sum exceeds kBlockSumMax (or no max is set yet) does
+// the wave take the cold path (rebase_block).  O / l is exact whatever the
+// reference is, since both use it.  Issue order: block 0's QK MFMAs; block
+// 1's QK MFMAs, with block 0's exponentials after each; block 0's PV MFMAs,
+// each followed by two of block 1's exponentials and the V^T reads of block
+// 1; block 1's PV MFMAs (sched_barrier keeps the groups in that order).
+template <class C>
+__device__ __forceinline__ void attend_tile(const unsigned char *kbuf, const unsigned char *vbuf,
+                                            const int (&kofs)[C::KS], const int (&vofs)[C::DT],
+                                            const bf16x8 (&qf)[C::KS], SoftState<C> &st_, bool need_mask, int thr,
+                                            float c) {
+    constexpr int NPV = 2 * C::DT;  // PV MFMAs per block
+    const f32x16 zero = {};
     f32x16 sacc[2];
     bf16x8 ka[2][C::KS];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[t][r] = 0.f;
-        const int r = 32 * t + pn;
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks)
-            ka[t][ks] = *reinterpret_cast<const bf16x8 *>(kt + r * C::ROWB + k_slot<C::CPR>(r, 2 * ks + hf) * 16);
-    }
+            ka[t][ks] = *reinterpret_cast<const bf16x8 *>(kbuf + kofs[ks] + t * 32 * C::ROWB);
+    __builtin_amdgcn_sched_barrier(0);
+    sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[0][0], qf[0], zero, 0, 0, 0);
 #pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks)
+    for (int ks = 1; ks < C::KS; ++ks)
         sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[0][ks], qf[ks], sacc[0], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
     if (need_mask) mask_block(sacc[0], 0, thr);
 
     // ---- block 1's QK MFMAs; block 0's probabilities
-    float mc = (m == -INFINITY) ? 0.f : m * c;
-    bf16x8 p0_lo, p0_hi, p1_lo, p1_hi;
+    f32x16 pf;
+    sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[1][0], qf[0], zero, 0, 0, 0);
 #pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks)
+    for (int ks = 1; ks < C::KS; ++ks)
         sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[1][ks], qf[ks], sacc[1], 0, 0, 0);
-    float ls = block_probs<C>(sacc[0], c, mc, p0_lo, p0_hi);
-    if (__builtin_expect(!m_set || __any(!(ls <= kBlockSumMax)), 0)) {
-        ls = rebase_block<C>(sacc[0], o, m, l, c, p0_lo, p0_hi);
-        m_set = true;
-        mc = (m == -INFINITY) ? 0.f : m * c;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) probs_step(sacc[0], c, st_.mc, i, pf);
+    bf16x8 p0_lo, p0_hi, p1_lo, p1_hi;
+    float ls = probs_finish(pf, p0_lo, p0_hi);
+    if (__builtin_expect(!st_.m_set || __any(!(ls <= kBlockSumMax)), 0)) {
+        ls = rebase_block<C>(sacc[0], st_.o, st_.m, st_.l, c, p0_lo, p0_hi);
+        st_.m_set = true;
+        st_.mc = (st_.m == -INFINITY) ? 0.f : st_.m * c;
     }
-    l += ls;
+    st_.l += ls;
     if (need_mask) mask_block(sacc[1], 1, thr);
 
-    // ---- block 0's PV MFMAs; block 1's probabilities
-    pv_group<C>(vt, vrd, 0, p0_lo, o);
-    pv_group<C>(vt, vrd, 1, p0_hi, o);
-    ls = block_probs<C>(sacc[1], c, mc, p1_lo, p1_hi);
-    if (__builtin_expect(__any(!(ls <= kBlockSumMax)), 0)) ls = rebase_block<C>(sacc[1], o, m, l, c, p1_lo, p1_hi);
-    l += ls;
+    // ---- block 0's PV MFMAs, block 1's probabilities and V^T reads between them
+    bf16x8 va0[NPV], va1[NPV];
+#pragma unroll
+    for (int k = 0; k < NPV; ++k) va0[k] = read_vt<C>(vbuf, vofs, k / C::DT, k % C::DT);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int k = 0; k < NPV; ++k) {
+        st_.o[k % C::DT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va0[k], k < C::DT ? p0_lo : p0_hi,
+                                                                  st_.o[k % C::DT], 0, 0, 0);
+        va1[k] = read_vt<C>(vbuf, vofs, 2 + k / C::DT, k % C::DT);
+#pragma unroll
+        for (int i = k * 8 / NPV; i < (k + 1) * 8 / NPV; ++i) probs_step(sacc[1], c, st_.mc, i, pf);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    ls = probs_finish(pf, p1_lo, p1_hi);
+    if (__builtin_expect(__any(!(ls <= kBlockSumMax)), 0)) {
+        ls = rebase_block<C>(sacc[1], st_.o, st_.m, st_.l, c, p1_lo, p1_hi);
+        st_.mc = (st_.m == -INFINITY) ? 0.f : st_.m * c;
+    }
+    st_.l += ls;
 
     // ---- block 1's PV MFMAs
-    pv_group<C>(vt, vrd, 2, p1_lo, o);
-    pv_group<C>(vt, vrd, 3, p1_hi, o);
+#pragma unroll
+    for (int k = 0; k < NPV; ++k)
+        st_.o[k % C::DT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va1[k], k < C::DT ? p1_lo : p1_hi,
+                                                                  st_.o[k % C::DT], 0, 0, 0);
 }
 
 template <int D, int NH>
 __global__ __launch_bounds__(kPfThreads, 1) void prefill_mfma_kernel(PfArgs a) {
     using C = Pf<D, NH>;
-    // [buffer][K, V][step rows]; after the key loop the same memory carries
-    // the second key half's partial results to the first
+    // [K, V][buffer][step rows]: every buffer and block offset of an LDS read
+    // is an immediate.  After the key loop the same memory carries the second
+    // key half's partial results to the first.
     __shared__ __attribute__((aligned(1024))) unsigned char s_kv[2][2][C::STEPB];
     __shared__ int s_blk[kBlkWin];
 
@@ -391,17 +472,23 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_mfma_kernel(PfArgs a) {
     const int64_t kv_row = (int64_t)a.hkv * D;  // elements per pool slot
     const int64_t kv_head = (int64_t)g * D;
     const int pn = swap_bits_2_3(n);
-    // byte offsets of this lane's V^T transpose reads within a tile, one per
-    // 32-wide d block: row 8hf + i/4, chunk (4dt + 2(grp&1) + (i&3)/2) ^ 4(i/4),
-    // byte 8(i&1) inside the chunk (i = lane%16, grp = lane/16)
-    int vrd[C::DT];
+    // byte offsets, from the K buffer of a step, of this lane's K reads (row
+    // pn of its key half's tile, chunk 2ks + hf, swizzled; block 1 adds 32
+    // rows, which keeps the swizzle) and V^T transpose reads (the V buffers
+    // start 2*STEPB further), one per 32-wide d block: row 8hf + i/4, chunk
+    // (4dt + 2(grp&1) + (i&3)/2) ^ 4(i/4), byte 8(i&1) inside the chunk (i =
+    // lane%16, grp = lane/16).  What remains of each LDS address is an
+    // immediate offset.
+    int kofs[C::KS], vofs[C::DT];
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) kofs[ks] = kh * C::TILEB + pn * C::ROWB + k_slot<C::CPR>(pn, 2 * ks + hf) * 16;
     {
         const int li = lane & 15, grp = lane >> 4;
         const int row = 8 * hf + (li >> 2);
 #pragma unroll
         for (int dt = 0; dt < C::DT; ++dt) {
             const int chunk = 4 * dt + 2 * (grp & 1) + ((li & 3) >> 1);
-            vrd[dt] = row * C::ROWB + v_slot<C::CPR>(row, chunk) * 16 + 8 * (li & 1);
+            vofs[dt] = 2 * C::STEPB + kh * C::TILEB + row * C::ROWB + v_slot<C::CPR>(row, chunk) * 16 + 8 * (li & 1);
         }
     }
     // byte offsets, inside the pool, of this lane's 16-byte pieces of the
@@ -451,13 +538,15 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_mfma_kernel(PfArgs a) {
                 qf[ks] = __builtin_bit_cast(bf16x8, v);
             }
         }
-        f32x16 o[C::DT];
+        SoftState<C> sm;
 #pragma unroll
         for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
-        float m = -INFINITY, l = 0.f;
-        bool m_set = false;  // wave-uniform: some block has set the reference max
+            for (int r = 0; r < 16; ++r) sm.o[dt][r] = 0.f;
+        sm.m = -INFINITY;
+        sm.mc = 0.f;
+        sm.l = 0.f;
+        sm.m_set = false;
 
         // block-id window staging (every thread reads ids only after a barrier)
         int win0 = 0;
@@ -473,12 +562,15 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_mfma_kernel(PfArgs a) {
         __syncthreads();
         const int blk0 = s_blk[0];  // physical block of key 0 (finite stand-in for masked rows)
         load_wave_rows<C>(a, 0, kmax_wg, shift, bmask, win0, blk0, kv_row, kv_head, koff, voff, w, lane, s_blk,
-                          s_kv[0][0], s_kv[0][1]);
+                          s_kv[0][0], s_kv[1][0]);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
 
-        for (int j = 0; j < nsteps; ++j) {
-            const int buf = j & 1;
+        // one step j in buffer BUF (compile-time): issue the loads of step
+        // j+1 into the other buffer, compute this wave's tile of step j, wait
+        // for the loads and synchronise
+        auto step = [&](int j, auto buf_c) {
+            constexpr int BUF = decltype(buf_c)::value;
             if (j + 1 < nsteps) {
                 const int kb1 = (j + 1) * kStep;
                 if ((min(kb1 + kStep - 1, kmax_wg) >> shift) >= win0 + kBlkWin) {  // leave the staged window
@@ -486,17 +578,18 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_mfma_kernel(PfArgs a) {
                     __syncthreads();
                 }
                 load_wave_rows<C>(a, kb1, kmax_wg, shift, bmask, win0, blk0, kv_row, kv_head, koff, voff, w,
-                                  lane, s_blk, s_kv[buf ^ 1][0], s_kv[buf ^ 1][1]);
+                                  lane, s_blk, s_kv[0][BUF ^ 1], s_kv[1][BUF ^ 1]);
             }
             const int kb = j * kStep + kh * kBN;
-            if (wave_active && kb <= kmax_w) {
-                const unsigned char *kt = s_kv[buf][0] + kh * C::TILEB;
-                const unsigned char *vt = s_kv[buf][1] + kh * C::TILEB;
-                const int thr = lim_me - kb - 8 * hf;
-                attend_tile<C>(kt, vt, qf, o, m, l, m_set, kb + kBN - 1 > kfull_w, thr, c, pn, hf, vrd);
-            }
+            if (wave_active && kb <= kmax_w)
+                attend_tile<C>(s_kv[0][BUF], s_kv[0][BUF], kofs, vofs, qf, sm, kb + kBN - 1 > kfull_w,
+                               lim_me - kb - 8 * hf, c);
             __builtin_amdgcn_s_waitcnt(0);  // this wave's direct loads of step j+1 have landed
             __syncthreads();
+        };
+        for (int j = 0; j < nsteps; j += 2) {
+            step(j, std::integral_constant<int, 0>{});
+            if (j + 1 < nsteps) step(j + 1, std::integral_constant<int, 1>{});
         }
 
         // ---- the second key half hands (O, m, l) to the first through LDS
@@ -504,18 +597,18 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_mfma_kernel(PfArgs a) {
 #pragma unroll
             for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) merge[(dt * 16 + r) * 64 + lane] = o[dt][r];
-            merge[(C::DT * 16) * 64 + lane] = m;
-            merge[(C::DT * 16 + 1) * 64 + lane] = l;
+                for (int r = 0; r < 16; ++r) merge[(dt * 16 + r) * 64 + lane] = sm.o[dt][r];
+            merge[(C::DT * 16) * 64 + lane] = sm.m;
+            merge[(C::DT * 16 + 1) * 64 + lane] = sm.l;
         }
         __syncthreads();
         if (kh == 0) {
             const float m2 = merge[(C::DT * 16) * 64 + lane];
             const float l2 = merge[(C::DT * 16 + 1) * 64 + lane];
-            const float mn = fmaxf(m, m2);
-            const float a1 = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m - mn) * c);
+            const float mn = fmaxf(sm.m, m2);
+            const float a1 = (sm.m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((sm.m - mn) * c);
             const float a2 = (m2 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m2 - mn) * c);
-            l = l * a1 + l2 * a2;
+            const float l = sm.l * a1 + l2 * a2;
             // ---- epilogue: O = O^T / l; lane (n, hf) holds d = 32dt + 8b + 4hf + a at register a + 4b
             const float l_tot = halves_sum(l);
             const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
@@ -528,7 +621,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_mfma_kernel(PfArgs a) {
 #pragma unroll
                         for (int a4 = 0; a4 < 4; ++a4) {
                             const int r = 4 * b + a4;
-                            v[a4] = (o[dt][r] * a1 + merge[(dt * 16 + r) * 64 + lane] * a2) * inv;
+                            v[a4] = (sm.o[dt][r] * a1 + merge[(dt * 16 + r) * 64 + lane] * a2) * inv;
                         }
                         *reinterpret_cast<bf16x4 *>(orow + 32 * dt + 8 * b + 4 * hf) = __builtin_convertvector(v, bf16x4);
                     }
