@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 1
+#define PA_ABI_VERSION 2
 
 typedef enum {
     PA_OK = 0,
@@ -147,6 +147,11 @@ pa_status pa_prefill_varlen(const void *q, int64_t q_row_stride, int32_t num_q_h
  *   block_table   int32 [num_seqs][block_table_stride].
  *   max_context_len  host upper bound of context_lens (sizes the launch).
  *   softmax_scale as for pa_prefill_varlen (finite, > 0).
+ *   row_order     NULL, or int32 [num_seqs]: a permutation of 0..num_seqs-1
+ *                 (precondition; pa_validate_decode_metadata checks a host
+ *                 copy) giving the order in which rows are scheduled, e.g.
+ *                 from pa_decode_order.  It changes the launch order only:
+ *                 outputs are bit-identical with or without it.
  *   out           [num_seqs][num_q_heads][head_dim] contiguous.
  *   workspace     >= pa_decode_workspace_bytes(...) bytes: split-K partial
  *                 results (running max, normaliser and fp32 accumulator per
@@ -157,8 +162,21 @@ pa_status pa_decode(const void *q, int64_t q_row_stride, int32_t num_q_heads,
                     const void *k_pool, const void *v_pool, const pa_pool *pool /* host */,
                     const int32_t *context_lens, const int32_t *block_table,
                     int32_t block_table_stride, int32_t num_seqs, int32_t max_context_len,
-                    float softmax_scale, void *out, void *workspace, size_t workspace_bytes,
-                    void *stream);
+                    float softmax_scale, const int32_t *row_order, void *out, void *workspace,
+                    size_t workspace_bytes, void *stream);
+
+/*
+ * pa_decode_order -- scheduling aid for pa_decode, not an operation of the
+ * pages: writes row_order (int32 [num_seqs], device) = the rows sorted by
+ * decreasing context_lens, ties by row index.  A decode step has the same
+ * context lengths in every layer, so one call per step serves all layers'
+ * pa_decode calls.  With ragged contexts and more (row, KV head) work items
+ * than the GPU runs at once, longest-first scheduling keeps a long row from
+ * running alone at the end of the launch.  num_seqs <= 2048 (else
+ * PA_ERR_UNSUPPORTED: pass row_order = NULL); 0 is a no-op.
+ */
+pa_status pa_decode_order(const int32_t *context_lens, int32_t num_seqs, int32_t *row_order,
+                          void *stream);
 
 /* Workspace sizes (bytes) for the matching calls with the same host sizes. */
 size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t total_q, int32_t num_q_heads,
@@ -187,7 +205,7 @@ pa_status pa_gather_kv(const void *k_pool, const void *v_pool, const pa_pool *po
  * == k_len, lengths within the maxima and the block table width, block ids of
  * every needed entry in range.  slot_mapping (may be NULL): ids in range or
  * -1, no duplicates.  Decode: 0 <= context_lens <= max_context_len, ids in
- * range.
+ * range; row_order (may be NULL) a permutation of the rows.
  */
 pa_status pa_validate_prefill_metadata(const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k,
                                        const int32_t *q_offsets, const int32_t *block_table,
@@ -198,7 +216,8 @@ pa_status pa_validate_prefill_metadata(const int32_t *cu_seqlens_q, const int32_
 pa_status pa_validate_decode_metadata(const int32_t *context_lens, const int32_t *block_table,
                                       int32_t block_table_stride, int32_t num_seqs,
                                       int32_t max_context_len, const int32_t *slot_mapping,
-                                      const pa_pool *pool, char *why, size_t why_len);
+                                      const int32_t *row_order, const pa_pool *pool, char *why,
+                                      size_t why_len);
 
 const char *pa_status_string(pa_status status);
 int pa_abi_version(void);

@@ -14,6 +14,7 @@ from ._lib import (  # noqa: F401
     PaPool,
     load,
     pa_decode,
+    pa_decode_order,
     pa_decode_workspace_bytes,
     pa_gather_kv,
     pa_prefill_varlen,

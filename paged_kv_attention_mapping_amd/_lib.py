@@ -25,7 +25,7 @@ _STATUS = {
 
 # Every symbol include/pa.h declares.
 EXPORTS = (
-    "pa_store_kv", "pa_prefill_varlen", "pa_decode", "pa_prefill_workspace_bytes",
+    "pa_store_kv", "pa_prefill_varlen", "pa_decode", "pa_decode_order", "pa_prefill_workspace_bytes",
     "pa_decode_workspace_bytes", "pa_gather_kv", "pa_validate_prefill_metadata",
     "pa_validate_decode_metadata", "pa_status_string", "pa_abi_version",
 )
@@ -60,18 +60,19 @@ def load() -> ctypes.CDLL:
     lib.pa_store_kv.argtypes = [p, i64, p, i64, p, i32, p, p, pool, p]
     lib.pa_prefill_varlen.argtypes = [p, i64, i32, p, p, pool, p, p, p, p, i32, i32, i32, i32, i32, f32,
                                       p, p, sz, p]
-    lib.pa_decode.argtypes = [p, i64, i32, p, p, pool, p, p, i32, i32, i32, f32, p, p, sz, p]
+    lib.pa_decode.argtypes = [p, i64, i32, p, p, pool, p, p, i32, i32, i32, f32, p, p, p, sz, p]
+    lib.pa_decode_order.argtypes = [p, i32, p, p]
     lib.pa_prefill_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, pool]
     lib.pa_prefill_workspace_bytes.restype = sz
     lib.pa_decode_workspace_bytes.argtypes = [i32, i32, i32, pool]
     lib.pa_decode_workspace_bytes.restype = sz
     lib.pa_gather_kv.argtypes = [p, p, pool, p, p, i32, i32, i32, p, p, p]
     lib.pa_validate_prefill_metadata.argtypes = [p, p, p, p, i32, i32, i32, i32, p, i32, pool, p, sz]
-    lib.pa_validate_decode_metadata.argtypes = [p, p, i32, i32, i32, p, pool, p, sz]
+    lib.pa_validate_decode_metadata.argtypes = [p, p, i32, i32, i32, p, p, pool, p, sz]
     lib.pa_status_string.argtypes = [i32]
     lib.pa_status_string.restype = ctypes.c_char_p
     lib.pa_abi_version.restype = ctypes.c_int
-    for fn in ("pa_store_kv", "pa_prefill_varlen", "pa_decode", "pa_gather_kv",
+    for fn in ("pa_store_kv", "pa_prefill_varlen", "pa_decode", "pa_decode_order", "pa_gather_kv",
                "pa_validate_prefill_metadata", "pa_validate_decode_metadata"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
@@ -194,8 +195,9 @@ def pa_prefill_varlen(q, k_pool, v_pool, cu_seqlens_q, cu_seqlens_k, q_offsets, 
 
 
 def pa_decode(q, k_pool, v_pool, context_lens, block_table, max_context_len, softmax_scale,
-              out=None, workspace=None):
-    """One query per sequence over its paged context; returns out [B, Hq, D]."""
+              out=None, workspace=None, row_order=None):
+    """One query per sequence over its paged context; returns out [B, Hq, D].
+    row_order: optional int32 device permutation of the rows (pa_decode_order)."""
     lib = load()
     _dev(q, k_pool, v_pool)
     pool = pool_desc(k_pool)
@@ -203,6 +205,10 @@ def pa_decode(q, k_pool, v_pool, context_lens, block_table, max_context_len, sof
     if d != pool.head_dim or q.dtype != k_pool.dtype:
         raise ValueError("q must match the pools' head_dim and dtype")
     context_lens, block_table = _i32(context_lens, "context_lens"), _i32(block_table, "block_table")
+    if row_order is not None:
+        row_order = _i32(row_order, "row_order")
+        if row_order.numel() != b:
+            raise ValueError("row_order must hold one entry per sequence")
     if out is None:
         out = torch.empty((b, hq, d), dtype=q.dtype, device=q.device)
     elif not out.is_contiguous() or out.shape != (b, hq, d) or out.dtype != q.dtype:
@@ -212,8 +218,22 @@ def pa_decode(q, k_pool, v_pool, context_lens, block_table, max_context_len, sof
     _check("pa_decode", lib.pa_decode(
         _ptr(q), _row_stride(q, hq * d, "q"), hq, _ptr(k_pool), _ptr(v_pool), ctypes.byref(pool),
         _ptr(context_lens), _ptr(block_table), block_table.shape[1], b, int(max_context_len),
-        float(softmax_scale), _ptr(out), _ptr(workspace), wbytes, _stream()))
+        float(softmax_scale), _ptr(row_order), _ptr(out), _ptr(workspace), wbytes, _stream()))
     return out
+
+
+def pa_decode_order(context_lens, row_order=None):
+    """Rows by decreasing context length (ties by index), as an int32 device
+    tensor for pa_decode's row_order; one call serves every layer of a step."""
+    lib = load()
+    context_lens = _i32(context_lens, "context_lens")
+    n = context_lens.numel()
+    if row_order is None:
+        row_order = torch.empty(n, dtype=torch.int32, device=context_lens.device)
+    elif row_order.dtype != torch.int32 or not row_order.is_contiguous() or row_order.numel() != n:
+        raise ValueError("row_order must be a contiguous int32 tensor of num_seqs entries")
+    _check("pa_decode_order", lib.pa_decode_order(_ptr(context_lens), n, _ptr(row_order), _stream()))
+    return row_order
 
 
 def pa_gather_kv(k_pool, v_pool, cu_seqlens_k, block_table, total_k):
@@ -255,13 +275,15 @@ def validate_prefill_metadata(cu_seqlens_q, cu_seqlens_k, q_offsets, block_table
         raise PaError("pa_validate_prefill_metadata", code, why.value.decode())
 
 
-def validate_decode_metadata(context_lens, block_table, max_context_len, pool: PaPool, slot_mapping=None):
+def validate_decode_metadata(context_lens, block_table, max_context_len, pool: PaPool, slot_mapping=None,
+                             row_order=None):
     lib = load()
-    cl, bt, sm = (_host_i32(x) for x in (context_lens, block_table, slot_mapping))
+    cl, bt, sm, ro = (_host_i32(x) for x in (context_lens, block_table, slot_mapping, row_order))
     why = ctypes.create_string_buffer(256)
     vp = ctypes.c_void_p
     code = lib.pa_validate_decode_metadata(
         cl.ctypes.data_as(vp), bt.ctypes.data_as(vp), bt.shape[1], len(cl), max_context_len,
-        None if sm is None else sm.ctypes.data_as(vp), ctypes.byref(pool), why, 256)
+        None if sm is None else sm.ctypes.data_as(vp), None if ro is None else ro.ctypes.data_as(vp),
+        ctypes.byref(pool), why, 256)
     if code != 0:
         raise PaError("pa_validate_decode_metadata", code, why.value.decode())

@@ -160,8 +160,8 @@ pa_status pa_prefill_varlen(const void *q, int64_t q_row_stride, int32_t num_q_h
 pa_status pa_decode(const void *q, int64_t q_row_stride, int32_t num_q_heads, const void *k_pool,
                     const void *v_pool, const pa_pool *pool, const int32_t *context_lens,
                     const int32_t *block_table, int32_t block_table_stride, int32_t num_seqs,
-                    int32_t max_context_len, float softmax_scale, void *out, void *workspace,
-                    size_t workspace_bytes, void *stream) {
+                    int32_t max_context_len, float softmax_scale, const int32_t *row_order, void *out,
+                    void *workspace, size_t workspace_bytes, void *stream) {
     pa::PoolGeom g;
     pa_status st = check_attention_shape(pool, num_q_heads, &g);
     if (st != PA_OK) return st;
@@ -179,8 +179,16 @@ pa_status pa_decode(const void *q, int64_t q_row_stride, int32_t num_q_heads, co
     const size_t need = pa::row_attention_workspace_bytes(plan, num_q_heads, g.d);
     if (need && (!workspace || workspace_bytes < need)) return PA_ERR_WORKSPACE;
     return from_hip(pa::launch_decode(q, q_row_stride, num_q_heads, k_pool, v_pool, g, context_lens,
-                                      block_table, block_table_stride, plan, softmax_scale, out,
-                                      workspace, (hipStream_t)stream));
+                                      block_table, block_table_stride, plan, softmax_scale, row_order,
+                                      out, workspace, (hipStream_t)stream));
+}
+
+pa_status pa_decode_order(const int32_t *context_lens, int32_t num_seqs, int32_t *row_order, void *stream) {
+    if (num_seqs < 0) return PA_ERR_BAD_SHAPE;
+    if (num_seqs == 0) return PA_OK;
+    if (!context_lens || !row_order) return PA_ERR_NULL_ARG;
+    if (num_seqs > pa::kDecodeOrderMax) return PA_ERR_UNSUPPORTED;
+    return from_hip(pa::launch_decode_order(context_lens, num_seqs, row_order, (hipStream_t)stream));
 }
 
 pa_status pa_gather_kv(const void *k_pool, const void *v_pool, const pa_pool *pool,
@@ -283,7 +291,8 @@ pa_status pa_validate_prefill_metadata(const int32_t *cu_seqlens_q, const int32_
 pa_status pa_validate_decode_metadata(const int32_t *context_lens, const int32_t *block_table,
                                       int32_t block_table_stride, int32_t num_seqs,
                                       int32_t max_context_len, const int32_t *slot_mapping,
-                                      const pa_pool *pool, char *why, size_t why_len) {
+                                      const int32_t *row_order, const pa_pool *pool, char *why,
+                                      size_t why_len) {
     if (why && why_len) why[0] = 0;
     if (!pool) return PA_ERR_NULL_ARG;
     if (num_seqs < 0) return PA_ERR_BAD_SHAPE;
@@ -297,6 +306,17 @@ pa_status pa_validate_decode_metadata(const int32_t *context_lens, const int32_t
         }
         pa_status st = check_table_row(block_table, block_table_stride, s, context_lens[s], pool, why, why_len);
         if (st != PA_OK) return st;
+    }
+    if (row_order) {  // a permutation of the rows
+        std::vector<char> seen((size_t)num_seqs, 0);
+        for (int32_t r = 0; r < num_seqs; ++r) {
+            const int32_t s = row_order[r];
+            if (s < 0 || s >= num_seqs || seen[(size_t)s]) {
+                say(why, why_len, "row_order[%lld] = %lld is out of range or repeated", r, s);
+                return PA_ERR_BAD_METADATA;
+            }
+            seen[(size_t)s] = 1;
+        }
     }
     return check_slots(slot_mapping, num_seqs, pool, why, why_len);
 }

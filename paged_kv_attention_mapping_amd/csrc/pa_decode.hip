@@ -25,6 +25,7 @@
 //
 // The same kernel also serves as the vector-ALU prefill path: a prefill row is
 // one packed query token whose context is min(q_offset + i + 1, k_len) keys.
+#include <limits.h>
 #include <math.h>
 
 #include "pa_device.h"
@@ -39,6 +40,7 @@ constexpr int kUnroll = 4;    // tokens per lane per round (K and V loads each)
 constexpr int kSplitMax = 1 << 20;   // keys per split, upper bound
 constexpr int kBlkIds = 4096;        // block ids a split may span (LDS staging)
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kOrderThreads = 1024;
 
 template <typename T, int D, int NW>
 struct RowCfg {
@@ -49,19 +51,51 @@ struct RowCfg {
     static_assert(LPT >= 1 && LPT <= kWave && kWave % LPT == 0, "head_dim");
 };
 
+// Decode rows.  `order`, when given, is a permutation of the rows: the
+// workgroups of row slot r (dispatched in index order) serve row order[r].
+// With the longest-first order of decode_order_kernel the long rows start
+// first and the short ones fill the end of the launch, instead of a long row
+// streaming on alone at the end.  Results do not depend on the order.
 struct DecodeRows {
     const int32_t *context_lens;
+    const int32_t *order;
+    __device__ __forceinline__ int row_of(int slot) const { return order ? order[slot] : slot; }
     __device__ __forceinline__ void get(int r, int &seq, int &ctx) const {
         seq = r;
         ctx = context_lens[r];
     }
 };
 
+// order[rank] = row, for the rows ranked by decreasing context length with
+// ties by row index (a strict total order, so every row gets its own rank).
+// One workgroup; n <= kDecodeOrderMax.
+__global__ __launch_bounds__(kOrderThreads) void decode_order_kernel(const int32_t *__restrict__ context_lens, int n,
+                                                                     int32_t *__restrict__ order) {
+    __shared__ __attribute__((aligned(16))) int s_len[kDecodeOrderMax];
+    const int n4 = (n + 3) & ~3;
+    for (int i = threadIdx.x; i < n4; i += kOrderThreads) s_len[i] = i < n ? context_lens[i] : INT_MIN;
+    __syncthreads();
+    for (int i = threadIdx.x; i < n; i += kOrderThreads) {
+        const int li = s_len[i];
+        int rank = 0;
+        for (int j = 0; j < n4; j += 4) {
+            const int4 v = *reinterpret_cast<const int4 *>(s_len + j);
+            // padding (INT_MIN at index >= n > i) never ranks ahead of row i
+            rank += (v.x > li) | ((v.x == li) & (j < i));
+            rank += (v.y > li) | ((v.y == li) & (j + 1 < i));
+            rank += (v.z > li) | ((v.z == li) & (j + 2 < i));
+            rank += (v.w > li) | ((v.w == li) & (j + 3 < i));
+        }
+        order[rank] = i;
+    }
+}
+
 struct PrefillRows {
     const int32_t *cu_q;
     const int32_t *cu_k;
     const int32_t *q_off;
     int num_seqs;
+    __device__ __forceinline__ int row_of(int slot) const { return slot; }
     __device__ __forceinline__ void get(int r, int &seq, int &ctx) const {
         int lo = 0, hi = num_seqs;  // cu_q[lo] <= r < cu_q[hi]
         while (hi - lo > 1) {
@@ -148,7 +182,7 @@ __global__ __launch_bounds__(NW * kWave) void row_attn_split(RowArgs a, Rows row
     const int g = (int)(wg % hkv);
     const int64_t rest = wg / hkv;
     const int split = (int)(rest % a.num_splits);
-    const int row = (int)(rest / a.num_splits);
+    const int row = rows.row_of((int)(rest / a.num_splits));
     int seq, ctx;
     rows.get(row, seq, ctx);
     // Never index past the table row or past the splits the launch covers.
@@ -514,10 +548,18 @@ size_t row_attention_workspace_bytes(const RowAttnPlan &p, int hq, int d) {
 hipError_t launch_decode(const void *q, int64_t q_row_stride, int hq, const void *k_pool,
                          const void *v_pool, const PoolGeom &g, const int32_t *context_lens,
                          const int32_t *block_table, int bt_stride, const RowAttnPlan &plan,
-                         float softmax_scale, void *out, void *workspace, hipStream_t stream) {
+                         float softmax_scale, const int32_t *row_order, void *out, void *workspace,
+                         hipStream_t stream) {
     const RowArgs a = make_args(q, q_row_stride, hq, k_pool, v_pool, g, block_table, bt_stride, plan,
                                 softmax_scale, out, workspace);
-    return dispatch(g, hq / g.hkv, plan.waves, a, DecodeRows{context_lens}, stream);
+    return dispatch(g, hq / g.hkv, plan.waves, a, DecodeRows{context_lens, row_order}, stream);
+}
+
+hipError_t launch_decode_order(const int32_t *context_lens, int num_rows, int32_t *row_order,
+                               hipStream_t stream) {
+    hipLaunchKernelGGL(decode_order_kernel, dim3(1), dim3(kOrderThreads), 0, stream, context_lens, num_rows,
+                       row_order);
+    return hipGetLastError();
 }
 
 hipError_t launch_prefill_rows(const void *q, int64_t q_row_stride, int hq, const void *k_pool,

@@ -45,7 +45,13 @@ size_t row_attention_workspace_bytes(const RowAttnPlan &p, int hq, int d);
 hipError_t launch_decode(const void *q, int64_t q_row_stride, int hq, const void *k_pool,
                          const void *v_pool, const PoolGeom &g, const int32_t *context_lens,
                          const int32_t *block_table, int bt_stride, const RowAttnPlan &plan,
-                         float softmax_scale, void *out, void *workspace, hipStream_t stream);
+                         float softmax_scale, const int32_t *row_order, void *out, void *workspace,
+                         hipStream_t stream);
+
+// Longest-context-first permutation of decode rows (one workgroup).
+constexpr int kDecodeOrderMax = 2048;
+hipError_t launch_decode_order(const int32_t *context_lens, int num_rows, int32_t *row_order,
+                               hipStream_t stream);
 
 hipError_t launch_prefill_rows(const void *q, int64_t q_row_stride, int hq, const void *k_pool,
                                const void *v_pool, const PoolGeom &g, const int32_t *cu_seqlens_q,

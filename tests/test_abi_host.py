@@ -28,7 +28,7 @@ def test_library_loads_and_exports_every_symbol():
     lib = pa.load()
     for name in _declared_symbols():
         assert hasattr(lib, name), name
-    assert lib.pa_abi_version() == 1
+    assert lib.pa_abi_version() == 2
     assert lib.pa_status_string(0) == b"ok"
     assert b"workspace" in lib.pa_status_string(5)
 
@@ -62,13 +62,19 @@ def test_host_argument_errors_return_before_launch():
     assert lib.pa_prefill_varlen(*args) == 2      # 3 % 2 != 0
     # decode: zero sequences is a no-op, nulls are rejected
     assert lib.pa_decode(None, 64, 4, None, None, ctypes.byref(pool), None, None, 1, 0, 0, 0.1,
-                         None, None, 0, None) == 0
+                         None, None, None, 0, None) == 0
     assert lib.pa_decode(None, 64, 4, None, None, ctypes.byref(pool), None, None, 1, 3, 10, 0.1,
-                         None, None, 0, None) == 1
+                         None, None, None, 0, None) == 1
+    # decode order: no-op, nulls, negative and too many rows
+    assert lib.pa_decode_order(None, 0, None, None) == 0
+    assert lib.pa_decode_order(None, 5, None, None) == 1
+    assert lib.pa_decode_order(None, -1, None, None) == 2
+    dummy = ctypes.c_void_p(16)  # never dereferenced: the size check comes first
+    assert lib.pa_decode_order(dummy, 2049, dummy, None) == 4
     # the softmax scale must be finite and positive (checked before any pointer)
     for scale in (0.0, -0.1, float("inf"), float("nan")):
         assert lib.pa_decode(None, 64, 4, None, None, ctypes.byref(pool), None, None, 1, 3, 10, scale,
-                             None, None, 0, None) == 2
+                             None, None, None, 0, None) == 2
         args = [None, 64, 4, None, None, ctypes.byref(pool), None, None, None, None, 1, 1, 1, 1, 1, scale,
                 None, None, 0, None]
         assert lib.pa_prefill_varlen(*args) == 2
@@ -93,7 +99,8 @@ def test_validators_accept_generated_metadata():
                                      np.concatenate([case.slot_cached, case.slot_new]))
     dec = W.c4_decode_layout()
     pool = pa.PaPool(dec.num_blocks, dec.block_size, dec.num_kv_heads, dec.head_dim, pa.PA_BF16)
-    pa.validate_decode_metadata(dec.context_lens, dec.block_table, dec.max_context_len, pool, dec.slot_new)
+    pa.validate_decode_metadata(dec.context_lens, dec.block_table, dec.max_context_len, pool, dec.slot_new,
+                                row_order=np.argsort(-dec.context_lens, kind="stable"))
 
 
 def test_validators_reject_bad_metadata():
@@ -115,3 +122,8 @@ def test_validators_reject_bad_metadata():
     pool = pa.PaPool(dec.num_blocks, dec.block_size, dec.num_kv_heads, dec.head_dim, pa.PA_BF16)
     with pytest.raises(pa.PaError, match="context_lens"):
         pa.validate_decode_metadata(dec.context_lens, dec.block_table, 1000, pool)
+    order = np.arange(len(dec.context_lens))
+    order[3] = order[4]  # a repeated row (and a missing one)
+    with pytest.raises(pa.PaError, match="row_order"):
+        pa.validate_decode_metadata(dec.context_lens, dec.block_table, dec.max_context_len, pool,
+                                    row_order=order)

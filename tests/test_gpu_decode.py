@@ -145,3 +145,46 @@ def test_batch_one_long_context_many_splits():
     say("[decode] batch 1 x 20000")
     out, ref = run_decode_host_case(case)
     assert max_abs_err(out, ref) <= tol("bf16")
+
+
+@pytest.mark.parametrize("num_rows", [600, 1100])
+def test_many_rows_with_ties_and_padding(num_rows):
+    """More (row, KV head) work items than run at once, lengths from a small
+    set (most rows tie) and every 7th row a padding row (context 0): the
+    longest-first order is the stable argsort of -context_lens, and decoding
+    with it gives the oracle's result, bit-identical to the given order."""
+    rng = np.random.default_rng(4100 + num_rows)
+    ctx = rng.choice([1, 16, 33, 64, 100, 255, 256, 300], size=num_rows)
+    ctx[::7] = 0
+    case = W.make_decode("ties", 4200 + num_rows, [int(c) for c in ctx], 16, 8, 64, 16, "bf16")
+    say(f"[decode] {num_rows} rows with ties and padding")
+    out, ref = run_decode_host_case(case)
+    assert max_abs_err(out, ref) <= tol("bf16")
+    g = as_f64(out)
+    assert (g[::7] == 0).all()
+    cl = to_dev(case.context_lens)
+    order = pa.pa_decode_order(cl)
+    torch.cuda.synchronize()
+    assert np.array_equal(order.cpu().numpy(), np.argsort(-case.context_lens, kind="stable"))
+    kp, vp = host_decode_pools(case)
+    oracle.store_kv(case.k_new, case.v_new, case.slot_new, kp, vp)
+    ordered = pa.pa_decode(to_dev(case.q), to_dev(kp), to_dev(vp), cl, to_dev(case.block_table),
+                           case.max_context_len, case.scale, row_order=order)
+    torch.cuda.synchronize()
+    assert to_host_bits(ordered).tobytes() == to_host_bits(out).tobytes()
+
+
+def test_c4_row_order_changes_nothing():
+    """C4 decoded in longest-first order equals the given order bit for bit."""
+    lay = W.c4_decode_layout()
+    say("[decode] C4 with and without row order")
+    kd = W.device_normal((lay.num_blocks, lay.block_size, lay.num_kv_heads, lay.head_dim), 7)
+    vd = W.device_normal((lay.num_blocks, lay.block_size, lay.num_kv_heads, lay.head_dim), 8)
+    q = W.device_normal((lay.num_seqs, lay.num_q_heads, lay.head_dim), 9)
+    cl, bt = to_dev(lay.context_lens), to_dev(lay.block_table)
+    base = pa.pa_decode(q, kd, vd, cl, bt, lay.max_context_len, lay.scale)
+    order = pa.pa_decode_order(cl)
+    ordered = pa.pa_decode(q, kd, vd, cl, bt, lay.max_context_len, lay.scale, row_order=order)
+    torch.cuda.synchronize()
+    assert np.array_equal(order.cpu().numpy(), np.argsort(-lay.context_lens, kind="stable"))
+    assert to_host_bits(ordered).tobytes() == to_host_bits(base).tobytes()
