@@ -143,3 +143,29 @@ def test_block_permutation_invariance_and_determinism():
     torch.cuda.synchronize()
     assert to_host_bits(again).tobytes() == to_host_bits(out).tobytes()
     assert max_abs_err(perm_out, ref) <= tol("bf16")
+
+
+@pytest.mark.parametrize("direction", ["rising", "falling"])
+def test_steep_score_ramp(direction):
+    """Every key's score is a ramp along the sequence spanning about 200 in
+    log2 units over 1024 keys (q = 40u, k_j = 40 (j/1024) u for a unit vector
+    u, or the ramp reversed): rising scores keep moving the softmax's running
+    reference past its bound, so its rescale path runs over and over; falling
+    scores make every later key underflow against the first block."""
+    case = W.make_prefill("ramp", 7100, [1024], [0], 16, 8, 128, 16, "bf16")
+    rng = np.random.default_rng(7101)
+    u = rng.standard_normal(128)
+    u /= np.linalg.norm(u)
+    ramp = 40.0 * np.arange(1024) / 1024.0
+    if direction == "falling":
+        ramp = ramp[::-1].copy()
+    case.q = W.f32_to_bf16_bits(np.broadcast_to(40.0 * u, (1024, 16, 128)).astype(np.float32))
+    case.k_new = W.f32_to_bf16_bits(
+        np.broadcast_to(ramp[:, None, None] * u[None, None, :], (1024, 8, 128)).astype(np.float32))
+    say(f"[prefill] steep {direction} score ramp")
+    rows = np.array([0, 1, 31, 32, 63, 64, 100, 511, 512, 767, 1000, 1023], np.int32)
+    got, ref, _ = run_prefill(case, rows=rows)
+    err = max_abs_err(got, ref)
+    say(f"  max-abs {err:.3e}")
+    assert np.isfinite(got.float().cpu().numpy()).all()
+    assert err <= tol("bf16")
