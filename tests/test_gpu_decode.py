@@ -188,3 +188,22 @@ def test_c4_row_order_changes_nothing():
     torch.cuda.synchronize()
     assert np.array_equal(order.cpu().numpy(), np.argsort(-lay.context_lens, kind="stable"))
     assert to_host_bits(ordered).tobytes() == to_host_bits(base).tobytes()
+
+
+@pytest.mark.parametrize("pad", [-1, 2**31 - 1])
+def test_table_padding_is_never_read(pad):
+    """Decode reads no block-table entry past a row's last needed block:
+    padding with -1 or a huge id changes no output bit."""
+    case = W.make_decode("pad", 7400, [1, 17, 300, 1000, 40], 16, 8, 128, 16, "bf16")
+    say(f"[decode] table padding {pad}")
+    out, ref = run_decode_host_case(case)
+    assert max_abs_err(out, ref) <= tol("bf16")
+    kp, vp = host_decode_pools(case)
+    oracle.store_kv(case.k_new, case.v_new, case.slot_new, kp, vp)
+    bt = case.block_table.copy()
+    for s, c in enumerate(case.context_lens):
+        bt[s, max(1, -(-int(c) // case.block_size)):] = pad
+    again = pa.pa_decode(to_dev(case.q), to_dev(kp), to_dev(vp), to_dev(case.context_lens), to_dev(bt),
+                         case.max_context_len, case.scale)
+    torch.cuda.synchronize()
+    assert to_host_bits(again).tobytes() == to_host_bits(out).tobytes()

@@ -169,3 +169,36 @@ def test_steep_score_ramp(direction):
     say(f"  max-abs {err:.3e}")
     assert np.isfinite(got.float().cpu().numpy()).all()
     assert err <= tol("bf16")
+
+
+def test_shared_prefix_blocks():
+    """Two sequences whose block tables point at the same physical blocks for
+    a 256-token cached prefix (read-only sharing, as reference-counted prefix
+    blocks are): each attends to the shared keys exactly as to its own.  The
+    second sequence's original prefix blocks stay NaN-poisoned and unused."""
+    case = W.make_prefill("shared", 7200, [40, 70], [256, 256], 16, 8, 128, 16, "bf16")
+    shared = 256 // 16
+    case.block_table[1, :shared] = case.block_table[0, :shared]
+    case.slot_cached = case.slot_cached[:256]
+    case.k_cached, case.v_cached = case.k_cached[:256], case.v_cached[:256]
+    say("[prefill] shared prefix blocks")
+    got, ref, _ = run_prefill(case)
+    assert max_abs_err(got, ref) <= tol("bf16")
+
+
+@pytest.mark.parametrize("pad", [-1, 2**31 - 1])
+def test_table_padding_is_never_read(pad):
+    """Entries of a block-table row past the sequence's last needed block
+    are never read: padding them with -1 or a huge id changes no output bit."""
+    case = W.make_prefill("pad", 7300, [5, 70, 300, 17], [0, 30, 0, 200], 16, 8, 128, 16, "bf16")
+    say(f"[prefill] table padding {pad}")
+    base, ref, (kp, vp, kd, vd, _) = run_prefill(case)
+    assert max_abs_err(base, ref) <= tol("bf16")
+    bt = case.block_table.copy()
+    for s, k in enumerate(case.k_lens):
+        bt[s, -(-k // case.block_size):] = pad
+    again = pa.pa_prefill_varlen(to_dev(case.q), kd, vd, to_dev(case.cu_seqlens_q), to_dev(case.cu_seqlens_k),
+                                 to_dev(np.asarray(case.q_offsets, np.int32)), to_dev(bt), case.max_seqlen_q,
+                                 case.max_seqlen_k, case.scale)
+    torch.cuda.synchronize()
+    assert to_host_bits(again).tobytes() == to_host_bits(base).tobytes()
