@@ -147,7 +147,7 @@ def test_batch_one_long_context_many_splits():
     assert max_abs_err(out, ref) <= tol("bf16")
 
 
-@pytest.mark.parametrize("num_rows", [600, 1100])
+@pytest.mark.parametrize("num_rows", [600, 601, 1100])
 def test_many_rows_with_ties_and_padding(num_rows):
     """More (row, KV head) work items than run at once, lengths from a small
     set (most rows tie) and every 7th row a padding row (context 0): the
