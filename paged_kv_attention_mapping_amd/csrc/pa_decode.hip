@@ -10,15 +10,16 @@
 // into segments; each segment keeps its own running max m, normaliser l and
 // fp32 accumulator; a second kernel merges the segments by log-sum-exp.
 //
-// Layout on gfx950: one workgroup (4 waves) per (row, KV head g, split).  A
+// Layout on gfx950: one workgroup (4, 8 or 16 waves, chosen by the planner)
+// per (row, KV head g, split).  A
 // token's K row for head g is head_dim contiguous elements; LPT lanes each
 // load 16 bytes of it, so a wave covers 64/LPT tokens per load instruction
 // (bf16, d=128: 16 lanes x 16 B = 256 B per token, 4 tokens per wave).  The G
 // query heads that share KV head g are all served from the same K/V bytes
 // (GQA reuse, fork Q&A Q3 section 2), so every K/V byte is read from HBM once.
-// One pass: each round a lane issues all its K and V loads together (8 + 8
-// 16-byte loads in flight), the scores are summed across the LPT lanes with
-// DPP row operations (bf16 q.k on v_dot2_f32_bf16), and a running max,
+// One pass: each round a lane issues all its K and V loads together (two
+// rounds in flight, 4 + 4 16-byte loads), the scores are summed across the
+// LPT lanes with DPP row operations (bf16 q.k on v_dot2_f32_bf16), and a running max,
 // normaliser and fp32 accumulator per lane group absorb the round (online
 // softmax in the log2 domain).  The groups of a wave and then the waves are
 // combined by log-sum-exp.  Block ids of a split are staged in LDS once.
@@ -36,7 +37,7 @@ namespace {
 
 constexpr int kNW = 4;        // waves per merge workgroup
 constexpr int kThreads = kNW * kWave;
-constexpr int kUnroll = 4;    // tokens per lane per round (K and V loads each)
+constexpr int kUnroll = 2;    // tokens per lane per round (K and V loads each)
 constexpr int kSplitMax = 1 << 20;   // keys per split, upper bound
 constexpr int kBlkIds = 4096;        // block ids a split may span (LDS staging)
 constexpr float kLog2e = 1.4426950408889634f;
