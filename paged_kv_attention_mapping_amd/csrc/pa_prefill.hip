@@ -144,13 +144,46 @@ __device__ __forceinline__ float halves_sum(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 
-// Buffer resource over `bytes` bytes from p: raw (stride 0) addressing with
-// 32-bit data format, the gfx9 default for untyped buffer loads.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void *p, int bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, bytes, 0x00020000);
+// Words of a buffer resource over `bytes` bytes from p (wave-uniform): raw
+// (stride 0) addressing with 32-bit data format, the gfx9 default for
+// untyped buffer loads.
+__device__ __forceinline__ i32x4 raw_rsrc(const void *p, uint32_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(p);
+    return (i32x4){__builtin_amdgcn_readfirstlane((int)(uint32_t)a),
+                   __builtin_amdgcn_readfirstlane((int)((a >> 32) & 0xffff)),
+                   __builtin_amdgcn_readfirstlane((int)bytes), 0x00020000};
 }
+
+// LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const unsigned char *p) {
+    return (uint32_t)(uintptr_t)(const lds_u8 *)p;
+}
+
+// Direct loads to LDS, 16 bytes per lane, lane i writing lds_base + 16 i.
+// They are issued from inline assembly so that the compiler does not track
+// them: it would otherwise make every later LDS read wait for them (it
+// cannot tell which buffer they fill).  The kernel orders them itself: an
+// s_waitcnt on all counters and a barrier separate every buffer's loads from
+// its reads, and its reuse from earlier reads.
+// (M0, which the two write, is used by nothing else in this file.)
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void buffer_lds16(i32x4 rsrc, uint32_t voff, int soff, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+                 :
+                 : "v"(voff), "s"(rsrc), "s"(soff), "s"(lds_base)
+                 : "memory", "m0");
+}
+__device__ __forceinline__ void global_lds16(const void *src, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(src), "s"(lds_base)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
 
 // Direct HBM/L2 -> LDS loads of this wave's 16 rows of one step (keys
 // kb_step + 16w .. +15) into the step buffers dk / dv.  Slot q of the wave's
@@ -178,17 +211,17 @@ __device__ __forceinline__ void load_wave_rows(const PfArgs &a, int kb_step, int
         if (p >= 0) {
             const int row_bytes = (int)(kv_row * 2);
             const int64_t sbase = ((((int64_t)p << shift) + (row0 & bmask)) * kv_row + kv_head) * 2;
-            const __amdgpu_buffer_rsrc_t rk =
+            const i32x4 rk =
                 raw_rsrc(reinterpret_cast<const unsigned char *>(a.k_pool) + sbase, kRowsPerWave * row_bytes);
-            const __amdgpu_buffer_rsrc_t rv =
+            const i32x4 rv =
                 raw_rsrc(reinterpret_cast<const unsigned char *>(a.v_pool) + sbase, kRowsPerWave * row_bytes);
+            const uint32_t lk = __builtin_amdgcn_readfirstlane(lds_addr(dk) + w * C::LPW * 1024);
+            const uint32_t lv = __builtin_amdgcn_readfirstlane(lds_addr(dv) + w * C::LPW * 1024);
 #pragma unroll
             for (int u = 0; u < C::LPW; ++u) {
-                const int dst = __builtin_amdgcn_readfirstlane((w * C::LPW + u) * 1024);
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void *)(dk + dst), 16,
-                                                         koff[u], u * C::RPI * row_bytes, 0, 0);
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void *)(dv + dst), 16, voff,
-                                                         u * C::RPI * row_bytes, 0, 0);
+                const int soff = __builtin_amdgcn_readfirstlane(u * C::RPI * row_bytes);
+                buffer_lds16(rk, koff[u], soff, lk + u * 1024);
+                buffer_lds16(rv, voff, soff, lv + u * 1024);
             }
             return;
         }
@@ -203,10 +236,10 @@ __device__ __forceinline__ void load_wave_rows(const PfArgs &a, int kb_step, int
         const int64_t slot = p >= 0 ? ((int64_t)p << shift) + (key & bmask)
                                     : (blk0 >= 0 ? ((int64_t)blk0 << shift) : 0);
         const int64_t eoff = slot * kv_row + kv_head;
-        __builtin_amdgcn_global_load_lds(a.k_pool + eoff + k_slot<C::CPR>(r, sl) * 8, dk + blk_i * 1024,
-                                         16, 0, 0);
-        __builtin_amdgcn_global_load_lds(a.v_pool + eoff + v_slot<C::CPR>(r, sl) * 8, dv + blk_i * 1024,
-                                         16, 0, 0);
+        global_lds16(a.k_pool + eoff + k_slot<C::CPR>(r, sl) * 8,
+                     __builtin_amdgcn_readfirstlane(lds_addr(dk) + blk_i * 1024));
+        global_lds16(a.v_pool + eoff + v_slot<C::CPR>(r, sl) * 8,
+                     __builtin_amdgcn_readfirstlane(lds_addr(dv) + blk_i * 1024));
     }
 }
 
@@ -430,6 +463,25 @@ __device__ __forceinline__ void attend_tile(const unsigned char *kbuf, const uns
                                                                   st_.o[k % C::DT], 0, 0, 0);
 }
 
+// One step of a wave: the direct loads of the next step into (nk, nv), if
+// `load`, then the wave's tile of this step from cur, if `tile`.  The three
+// step buffers are distinct (restrict), which tells the compiler that the
+// tile's LDS reads do not depend on the loads in flight: it then issues them
+// without waiting for those loads (the caller's s_waitcnt and barrier after
+// the step order every buffer's loads before its reads).
+template <class C>
+__device__ __forceinline__ void load_and_attend(const PfArgs &a, bool load, int kb1, int kmax, int shift, int bmask,
+                                                int win0, int blk0, int64_t kv_row, int64_t kv_head,
+                                                const uint32_t (&koff)[C::LPW], uint32_t voff, int w, int lane,
+                                                const int *s_blk, unsigned char *__restrict__ nk,
+                                                unsigned char *__restrict__ nv, bool tile,
+                                                const unsigned char *__restrict__ cur, const int (&kofs)[C::KS],
+                                                const int (&vofs)[C::DT], const bf16x8 (&qf)[C::KS],
+                                                SoftState<C> &st, bool need_mask, int thr, float c) {
+    if (load) load_wave_rows<C>(a, kb1, kmax, shift, bmask, win0, blk0, kv_row, kv_head, koff, voff, w, lane, s_blk, nk, nv);
+    if (tile) attend_tile<C>(cur, cur, kofs, vofs, qf, st, need_mask, thr, c);
+}
+
 template <int D, int NH>
 __global__ __launch_bounds__(kPfThreads, 1) void prefill_mfma_kernel(PfArgs a) {
     using C = Pf<D, NH>;
@@ -571,19 +623,16 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_mfma_kernel(PfArgs a) {
         // for the loads and synchronise
         auto step = [&](int j, auto buf_c) {
             constexpr int BUF = decltype(buf_c)::value;
-            if (j + 1 < nsteps) {
-                const int kb1 = (j + 1) * kStep;
-                if ((min(kb1 + kStep - 1, kmax_wg) >> shift) >= win0 + kBlkWin) {  // leave the staged window
-                    stage_ids(kb1 >> shift);
-                    __syncthreads();
-                }
-                load_wave_rows<C>(a, kb1, kmax_wg, shift, bmask, win0, blk0, kv_row, kv_head, koff, voff, w,
-                                  lane, s_blk, s_kv[0][BUF ^ 1], s_kv[1][BUF ^ 1]);
+            const bool load = j + 1 < nsteps;
+            const int kb1 = (j + 1) * kStep;
+            if (load && (min(kb1 + kStep - 1, kmax_wg) >> shift) >= win0 + kBlkWin) {  // leave the staged window
+                stage_ids(kb1 >> shift);
+                __syncthreads();
             }
             const int kb = j * kStep + kh * kBN;
-            if (wave_active && kb <= kmax_w)
-                attend_tile<C>(s_kv[0][BUF], s_kv[0][BUF], kofs, vofs, qf, sm, kb + kBN - 1 > kfull_w,
-                               lim_me - kb - 8 * hf, c);
+            load_and_attend<C>(a, load, kb1, kmax_wg, shift, bmask, win0, blk0, kv_row, kv_head, koff, voff, w, lane,
+                               s_blk, s_kv[0][BUF ^ 1], s_kv[1][BUF ^ 1], wave_active && kb <= kmax_w, s_kv[0][BUF],
+                               kofs, vofs, qf, sm, kb + kBN - 1 > kfull_w, lim_me - kb - 8 * hf, c);
             __builtin_amdgcn_s_waitcnt(0);  // this wave's direct loads of step j+1 have landed
             __syncthreads();
         };
