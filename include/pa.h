@@ -51,20 +51,20 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 2
+#define PA_ABI_VERSION 3
 
 typedef enum {
     PA_OK = 0,
     PA_ERR_NULL_ARG = 1,     /* a required pointer is NULL                      */
     PA_ERR_BAD_SHAPE = 2,    /* a size or stride is negative or inconsistent    */
-    PA_ERR_BAD_DTYPE = 3,    /* dtype is not PA_F32 / PA_BF16                   */
+    PA_ERR_BAD_DTYPE = 3,    /* dtype not supported by this call                */
     PA_ERR_UNSUPPORTED = 4,  /* head_dim, block_size or group size not built    */
     PA_ERR_WORKSPACE = 5,    /* workspace NULL or smaller than the *_bytes call */
     PA_ERR_HIP = 6,          /* a kernel launch failed                          */
     PA_ERR_BAD_METADATA = 7  /* (validators only) host copy of metadata invalid */
 } pa_status;
 
-typedef enum { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
+typedef enum { PA_F32 = 0, PA_BF16 = 1, PA_INT8 = 2 } pa_dtype;
 
 /* Shape of one layer's K pool (the V pool has the same shape). Host struct. */
 typedef struct {
@@ -93,6 +93,69 @@ pa_status pa_store_kv(const void *k, int64_t k_row_stride,
                       const int32_t *slot_mapping, int32_t num_tokens,
                       void *k_pool, void *v_pool, const pa_pool *pool /* host */,
                       void *stream);
+
+/*
+ * INT8 KV cache (LLM inference interview notes (nano-vllm fork), Q3: how
+ * quantization and dequantization are done).  An INT8 layer has, per K and
+ * per V, a code pool and a scale pool indexed by the same slot:
+ *   codes   int8    [num_blocks][block_size][num_kv_heads][head_dim]
+ *   scales  float16 [num_blocks][block_size][num_kv_heads]  (IEEE binary16)
+ * described by a pa_pool with dtype PA_INT8.  One (token, KV head) takes
+ * head_dim + 2 bytes (130 B at head_dim 128, against 256 B in bf16).
+ *
+ * pa_store_kv_int8 -- quantize this step's K/V rows into INT8 pools (part 1
+ * of that answer: quantization happens on write, inside the store).  For
+ * each token t with slot_mapping[t] != -1 and each KV head h, over the
+ * head_dim values x of that head:
+ *   scale   = max(max_i |x_i| / 127, 1e-8)     fp32; IEEE division
+ *   code_i  = trunc(x_i / scale + 0.5)  if x_i / scale >= 0
+ *             trunc(x_i / scale - 0.5)  otherwise            (fp32)
+ * and the scale is stored as fp16 (round to nearest even; 1e-8 and other
+ * scales below fp16's range store as 0, whose codes are all 0 anyway).
+ *
+ *   k, v          [num_tokens][num_kv_heads][head_dim] rows of src_dtype
+ *                 (PA_BF16 or PA_F32), strides in elements as in pa_store_kv;
+ *                 values must be finite and |x| <= 65504 * 127.
+ *   slot_mapping  int32 [num_tokens]; -1 = padding token, skipped.
+ *   k_pool,v_pool int8 code pools, 8-byte aligned; k_scale,v_scale fp16
+ *                 scale pools; all written in place.
+ *   pool          dtype PA_INT8; head_dim a multiple of 8, at most 256.
+ * Errors: PA_ERR_BAD_DTYPE (pool not PA_INT8, src_dtype not bf16/fp32),
+ * PA_ERR_UNSUPPORTED (head_dim, block_size, misaligned pools), the checks of
+ * pa_store_kv otherwise.  Slots must be unique within one call.
+ */
+pa_status pa_store_kv_int8(const void *k, int64_t k_row_stride,
+                           const void *v, int64_t v_row_stride, int32_t src_dtype,
+                           const int32_t *slot_mapping, int32_t num_tokens,
+                           void *k_pool, void *v_pool, void *k_scale, void *v_scale,
+                           const pa_pool *pool /* host */, void *stream);
+
+/*
+ * pa_decode_int8 -- pa_decode over INT8 pools, with the dequantization fused
+ * into the attention (the same answer, part 2: K/V are read as int8, widened
+ * and scaled in registers; no float copy of the cache is made).  It computes
+ * pa_decode's result with K and V replaced by their dequantized values
+ * code * float(scale).  As the pages suggest, the K scale multiplies each
+ * finished dot product and the V scale is folded into the probability.
+ *
+ *   q, out        [num_seqs][num_q_heads][head_dim] of q_dtype (PA_BF16 or
+ *                 PA_F32); q rows at q_row_stride elements, 16-byte aligned.
+ *   k_pool,v_pool int8 code pools, 16-byte aligned; k_scale,v_scale fp16
+ *                 scale pools (layout above); pool->dtype PA_INT8.
+ *   everything else as pa_decode (context_lens, block_table, row_order,
+ *                 workspace from pa_decode_int8_workspace_bytes).
+ * Query groups (num_q_heads / num_kv_heads) of 1, 2 or 4; head_dim 32, 64,
+ * 128 or 256 (else PA_ERR_UNSUPPORTED).  Errors as pa_decode.
+ */
+size_t pa_decode_int8_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                      int32_t max_context_len, const pa_pool *pool /* host */);
+pa_status pa_decode_int8(const void *q, int64_t q_row_stride, int32_t num_q_heads, int32_t q_dtype,
+                         const void *k_pool, const void *v_pool,
+                         const void *k_scale, const void *v_scale, const pa_pool *pool /* host */,
+                         const int32_t *context_lens, const int32_t *block_table,
+                         int32_t block_table_stride, int32_t num_seqs, int32_t max_context_len,
+                         float softmax_scale, const int32_t *row_order, void *out,
+                         void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * pa_prefill_varlen -- causal attention for a packed variable-length batch

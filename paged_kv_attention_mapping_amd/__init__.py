@@ -10,17 +10,22 @@ from ._lib import (  # noqa: F401
     LIB_PATH,
     PA_BF16,
     PA_F32,
+    PA_INT8,
     PaError,
     PaPool,
     load,
     pa_decode,
+    pa_decode_int8,
+    pa_decode_int8_workspace_bytes,
     pa_decode_order,
     pa_decode_workspace_bytes,
     pa_gather_kv,
     pa_prefill_varlen,
     pa_prefill_workspace_bytes,
     pa_store_kv,
+    pa_store_kv_int8,
     pool_desc,
+    pool_desc_int8,
     validate_decode_metadata,
     validate_prefill_metadata,
 )

@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(_PKG, "libpa.so")
 
 PA_F32 = 0
 PA_BF16 = 1
+PA_INT8 = 2
 
 _STATUS = {
     0: "PA_OK", 1: "PA_ERR_NULL_ARG", 2: "PA_ERR_BAD_SHAPE", 3: "PA_ERR_BAD_DTYPE",
@@ -25,7 +26,9 @@ _STATUS = {
 
 # Every symbol include/pa.h declares.
 EXPORTS = (
-    "pa_store_kv", "pa_prefill_varlen", "pa_decode", "pa_decode_order", "pa_prefill_workspace_bytes",
+    "pa_store_kv", "pa_store_kv_int8", "pa_prefill_varlen", "pa_decode", "pa_decode_int8",
+    "pa_decode_int8_workspace_bytes", "pa_decode_order",
+    "pa_prefill_workspace_bytes",
     "pa_decode_workspace_bytes", "pa_gather_kv", "pa_validate_prefill_metadata",
     "pa_validate_decode_metadata", "pa_status_string", "pa_abi_version",
 )
@@ -58,9 +61,13 @@ def load() -> ctypes.CDLL:
     p, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
     pool = ctypes.POINTER(PaPool)
     lib.pa_store_kv.argtypes = [p, i64, p, i64, p, i32, p, p, pool, p]
+    lib.pa_store_kv_int8.argtypes = [p, i64, p, i64, i32, p, i32, p, p, p, p, pool, p]
     lib.pa_prefill_varlen.argtypes = [p, i64, i32, p, p, pool, p, p, p, p, i32, i32, i32, i32, i32, f32,
                                       p, p, sz, p]
     lib.pa_decode.argtypes = [p, i64, i32, p, p, pool, p, p, i32, i32, i32, f32, p, p, p, sz, p]
+    lib.pa_decode_int8.argtypes = [p, i64, i32, i32, p, p, p, p, pool, p, p, i32, i32, i32, f32, p, p, p, sz, p]
+    lib.pa_decode_int8_workspace_bytes.argtypes = [i32, i32, i32, pool]
+    lib.pa_decode_int8_workspace_bytes.restype = sz
     lib.pa_decode_order.argtypes = [p, i32, p, p]
     lib.pa_prefill_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, pool]
     lib.pa_prefill_workspace_bytes.restype = sz
@@ -72,7 +79,7 @@ def load() -> ctypes.CDLL:
     lib.pa_status_string.argtypes = [i32]
     lib.pa_status_string.restype = ctypes.c_char_p
     lib.pa_abi_version.restype = ctypes.c_int
-    for fn in ("pa_store_kv", "pa_prefill_varlen", "pa_decode", "pa_decode_order", "pa_gather_kv",
+    for fn in ("pa_store_kv", "pa_store_kv_int8", "pa_prefill_varlen", "pa_decode", "pa_decode_int8", "pa_decode_order", "pa_gather_kv",
                "pa_validate_prefill_metadata", "pa_validate_decode_metadata"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
@@ -94,6 +101,17 @@ def pool_desc(k_pool: torch.Tensor) -> PaPool:
         raise ValueError("pools must be contiguous [num_blocks, block_size, num_kv_heads, head_dim]")
     nb, bs, hkv, d = k_pool.shape
     return PaPool(nb, bs, hkv, d, _dtype_code(k_pool))
+
+
+def pool_desc_int8(k_pool: torch.Tensor, k_scale: torch.Tensor) -> PaPool:
+    """Descriptor of an INT8 layer: int8 codes [NB, bs, Hkv, D] and float16
+    scales [NB, bs, Hkv], both contiguous."""
+    if k_pool.dim() != 4 or not k_pool.is_contiguous() or k_pool.dtype != torch.int8:
+        raise ValueError("INT8 pools must be contiguous int8 [num_blocks, block_size, num_kv_heads, head_dim]")
+    nb, bs, hkv, d = k_pool.shape
+    if k_scale.shape != (nb, bs, hkv) or k_scale.dtype != torch.float16 or not k_scale.is_contiguous():
+        raise ValueError("INT8 scales must be contiguous float16 [num_blocks, block_size, num_kv_heads]")
+    return PaPool(nb, bs, hkv, d, PA_INT8)
 
 
 def _dev(*ts):
@@ -194,6 +212,29 @@ def pa_prefill_varlen(q, k_pool, v_pool, cu_seqlens_q, cu_seqlens_k, q_offsets, 
     return out
 
 
+def pa_store_kv_int8(k, v, slot_mapping, k_pool, v_pool, k_scale, v_scale):
+    """Quantize k/v [T, Hkv, D] (bf16 or fp32) per (token, KV head) into the
+    INT8 code pools and fp16 scale pools at slot_mapping (int32, -1 = skip)."""
+    lib = load()
+    _dev(k, v, k_pool, v_pool, k_scale, v_scale)
+    pool = pool_desc_int8(k_pool, k_scale)
+    if v_pool.shape != k_pool.shape or v_pool.dtype != torch.int8 or not v_pool.is_contiguous():
+        raise ValueError("v_pool must match k_pool")
+    if v_scale.shape != k_scale.shape or v_scale.dtype != torch.float16 or not v_scale.is_contiguous():
+        raise ValueError("v_scale must match k_scale")
+    if k.dtype != v.dtype:
+        raise TypeError("k and v must have the same dtype")
+    row = pool.num_kv_heads * pool.head_dim
+    slot_mapping = _i32(slot_mapping, "slot_mapping")
+    n = slot_mapping.numel()
+    if k.shape[0] != n or v.shape[0] != n:
+        raise ValueError("k, v and slot_mapping must have the same number of tokens")
+    _check("pa_store_kv_int8", lib.pa_store_kv_int8(
+        _ptr(k), _row_stride(k, row, "k"), _ptr(v), _row_stride(v, row, "v"), _dtype_code(k),
+        _ptr(slot_mapping), n, _ptr(k_pool), _ptr(v_pool), _ptr(k_scale), _ptr(v_scale),
+        ctypes.byref(pool), _stream()))
+
+
 def pa_decode(q, k_pool, v_pool, context_lens, block_table, max_context_len, softmax_scale,
               out=None, workspace=None, row_order=None):
     """One query per sequence over its paged context; returns out [B, Hq, D].
@@ -219,6 +260,44 @@ def pa_decode(q, k_pool, v_pool, context_lens, block_table, max_context_len, sof
         _ptr(q), _row_stride(q, hq * d, "q"), hq, _ptr(k_pool), _ptr(v_pool), ctypes.byref(pool),
         _ptr(context_lens), _ptr(block_table), block_table.shape[1], b, int(max_context_len),
         float(softmax_scale), _ptr(row_order), _ptr(out), _ptr(workspace), wbytes, _stream()))
+    return out
+
+
+def pa_decode_int8_workspace_bytes(num_seqs, num_q_heads, max_context_len, k_pool, k_scale) -> int:
+    pool = pool_desc_int8(k_pool, k_scale)
+    return int(load().pa_decode_int8_workspace_bytes(num_seqs, num_q_heads, int(max_context_len),
+                                                     ctypes.byref(pool)))
+
+
+def pa_decode_int8(q, k_pool, v_pool, k_scale, v_scale, context_lens, block_table, max_context_len,
+                   softmax_scale, out=None, workspace=None, row_order=None):
+    """pa_decode over INT8 pools (int8 codes, fp16 scales); q/out bf16 or fp32."""
+    lib = load()
+    _dev(q, k_pool, v_pool, k_scale, v_scale)
+    pool = pool_desc_int8(k_pool, k_scale)
+    if v_pool.shape != k_pool.shape or v_pool.dtype != torch.int8 or not v_pool.is_contiguous():
+        raise ValueError("v_pool must match k_pool")
+    if v_scale.shape != k_scale.shape or v_scale.dtype != torch.float16 or not v_scale.is_contiguous():
+        raise ValueError("v_scale must match k_scale")
+    b, hq, d = q.shape
+    if d != pool.head_dim:
+        raise ValueError("q must match the pools' head_dim")
+    context_lens, block_table = _i32(context_lens, "context_lens"), _i32(block_table, "block_table")
+    if row_order is not None:
+        row_order = _i32(row_order, "row_order")
+        if row_order.numel() != b:
+            raise ValueError("row_order must hold one entry per sequence")
+    if out is None:
+        out = torch.empty((b, hq, d), dtype=q.dtype, device=q.device)
+    elif not out.is_contiguous() or out.shape != (b, hq, d) or out.dtype != q.dtype:
+        raise ValueError("out must be contiguous [B, Hq, D] of q's dtype")
+    nbytes = pa_decode_int8_workspace_bytes(b, hq, max_context_len, k_pool, k_scale)
+    workspace, wbytes = _workspace(nbytes, workspace, q.device)
+    _check("pa_decode_int8", lib.pa_decode_int8(
+        _ptr(q), _row_stride(q, hq * d, "q"), hq, _dtype_code(q), _ptr(k_pool), _ptr(v_pool), _ptr(k_scale),
+        _ptr(v_scale), ctypes.byref(pool), _ptr(context_lens), _ptr(block_table), block_table.shape[1], b,
+        int(max_context_len), float(softmax_scale), _ptr(row_order), _ptr(out), _ptr(workspace), wbytes,
+        _stream()))
     return out
 
 

@@ -42,6 +42,17 @@ pa_status check_pool(const pa_pool *pool, pa::PoolGeom *g) {
     return PA_OK;
 }
 
+// INT8 pools: the same geometry checks for dtype PA_INT8.
+pa_status check_pool_int8(const pa_pool *pool, pa::PoolGeom *g) {
+    if (!pool) return PA_ERR_NULL_ARG;
+    if (pool->dtype != PA_INT8) return PA_ERR_BAD_DTYPE;
+    pa_pool p = *pool;
+    p.dtype = PA_BF16;  // geometry only
+    pa_status st = check_pool(&p, g);
+    g->dtype = PA_INT8;
+    return st;
+}
+
 pa_status check_attention_shape(const pa_pool *pool, int32_t num_q_heads, pa::PoolGeom *g) {
     pa_status st = check_pool(pool, g);
     if (st != PA_OK) return st;
@@ -96,6 +107,25 @@ pa_status pa_store_kv(const void *k, int64_t k_row_stride, const void *v, int64_
     if (k_row_stride < row || v_row_stride < row) return PA_ERR_BAD_SHAPE;
     return from_hip(pa::launch_store_kv(k, k_row_stride, v, v_row_stride, slot_mapping, num_tokens,
                                         k_pool, v_pool, g, (hipStream_t)stream));
+}
+
+pa_status pa_store_kv_int8(const void *k, int64_t k_row_stride, const void *v, int64_t v_row_stride,
+                           int32_t src_dtype, const int32_t *slot_mapping, int32_t num_tokens, void *k_pool,
+                           void *v_pool, void *k_scale, void *v_scale, const pa_pool *pool, void *stream) {
+    pa::PoolGeom g;
+    pa_status st = check_pool_int8(pool, &g);
+    if (st != PA_OK) return st;
+    if (src_dtype != PA_F32 && src_dtype != PA_BF16) return PA_ERR_BAD_DTYPE;
+    if (num_tokens < 0) return PA_ERR_BAD_SHAPE;
+    if (g.d % 8 || g.d > 256) return PA_ERR_UNSUPPORTED;
+    if (num_tokens == 0) return PA_OK;
+    if (!k || !v || !slot_mapping || !k_pool || !v_pool || !k_scale || !v_scale) return PA_ERR_NULL_ARG;
+    const int64_t row = (int64_t)g.hkv * g.d;
+    if (k_row_stride < row || v_row_stride < row) return PA_ERR_BAD_SHAPE;
+    if ((reinterpret_cast<uintptr_t>(k_pool) | reinterpret_cast<uintptr_t>(v_pool)) & 7) return PA_ERR_UNSUPPORTED;
+    if ((reinterpret_cast<uintptr_t>(k_scale) | reinterpret_cast<uintptr_t>(v_scale)) & 1) return PA_ERR_UNSUPPORTED;
+    return from_hip(pa::launch_store_kv_int8(k, k_row_stride, v, v_row_stride, src_dtype, slot_mapping, num_tokens,
+                                             k_pool, v_pool, k_scale, v_scale, g, (hipStream_t)stream));
 }
 
 size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t total_q, int32_t num_q_heads,
@@ -181,6 +211,58 @@ pa_status pa_decode(const void *q, int64_t q_row_stride, int32_t num_q_heads, co
     return from_hip(pa::launch_decode(q, q_row_stride, num_q_heads, k_pool, v_pool, g, context_lens,
                                       block_table, block_table_stride, plan, softmax_scale, row_order,
                                       out, workspace, (hipStream_t)stream));
+}
+
+// INT8 decode: the bf16/fp32 decode's checks, with int8 code pools, fp16 scale
+// pools and q / out of q_dtype; query groups of 1, 2 or 4.
+pa_status check_decode_int8_shape(const pa_pool *pool, int32_t num_q_heads, int32_t q_dtype, pa::PoolGeom *g) {
+    pa_status st = check_pool_int8(pool, g);
+    if (st != PA_OK) return st;
+    if (q_dtype != PA_F32 && q_dtype != PA_BF16) return PA_ERR_BAD_DTYPE;
+    if (num_q_heads <= 0 || num_q_heads % g->hkv) return PA_ERR_BAD_SHAPE;
+    const int group = num_q_heads / g->hkv;
+    if (group != 1 && group != 2 && group != 4) return PA_ERR_UNSUPPORTED;
+    if (g->d != 32 && g->d != 64 && g->d != 128 && g->d != 256) return PA_ERR_UNSUPPORTED;
+    if (g->num_blocks < 1) return PA_ERR_BAD_SHAPE;
+    return PA_OK;
+}
+
+size_t pa_decode_int8_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,
+                                      const pa_pool *pool) {
+    pa::PoolGeom g;
+    if (check_decode_int8_shape(pool, num_q_heads, PA_BF16, &g) != PA_OK) return 0;
+    if (num_seqs <= 0 || max_context_len <= 0) return 0;
+    const pa::RowAttnPlan plan = pa::plan_row_attention(num_seqs, g, num_q_heads / g.hkv, max_context_len);
+    return pa::row_attention_workspace_bytes(plan, num_q_heads, g.d);
+}
+
+pa_status pa_decode_int8(const void *q, int64_t q_row_stride, int32_t num_q_heads, int32_t q_dtype,
+                         const void *k_pool, const void *v_pool, const void *k_scale, const void *v_scale,
+                         const pa_pool *pool, const int32_t *context_lens, const int32_t *block_table,
+                         int32_t block_table_stride, int32_t num_seqs, int32_t max_context_len, float softmax_scale,
+                         const int32_t *row_order, void *out, void *workspace, size_t workspace_bytes,
+                         void *stream) {
+    pa::PoolGeom g;
+    pa_status st = check_decode_int8_shape(pool, num_q_heads, q_dtype, &g);
+    if (st != PA_OK) return st;
+    if (num_seqs < 0 || max_context_len < 0) return PA_ERR_BAD_SHAPE;
+    if (!scale_ok(softmax_scale)) return PA_ERR_BAD_SHAPE;
+    if (num_seqs == 0) return PA_OK;
+    if (!q || !k_pool || !v_pool || !k_scale || !v_scale || !context_lens || !block_table || !out)
+        return PA_ERR_NULL_ARG;
+    if (block_table_stride <= 0) return PA_ERR_BAD_SHAPE;
+    if (q_row_stride < (int64_t)num_q_heads * g.d) return PA_ERR_BAD_SHAPE;
+    const int eb = elem_bytes(q_dtype);
+    if (!aligned16(q) || (q_row_stride * eb) % 16 || !aligned16(k_pool) || !aligned16(v_pool) ||
+        ((reinterpret_cast<uintptr_t>(k_scale) | reinterpret_cast<uintptr_t>(v_scale)) & 1))
+        return PA_ERR_UNSUPPORTED;
+    const int group = num_q_heads / g.hkv;
+    const pa::RowAttnPlan plan = pa::plan_row_attention(num_seqs, g, group, max_context_len);
+    const size_t need = pa::row_attention_workspace_bytes(plan, num_q_heads, g.d);
+    if (need && (!workspace || workspace_bytes < need)) return PA_ERR_WORKSPACE;
+    return from_hip(pa::launch_decode_int8(q, q_row_stride, num_q_heads, q_dtype, k_pool, v_pool, k_scale, v_scale,
+                                           g, context_lens, block_table, block_table_stride, plan, softmax_scale,
+                                           row_order, out, workspace, (hipStream_t)stream));
 }
 
 pa_status pa_decode_order(const int32_t *context_lens, int32_t num_seqs, int32_t *row_order, void *stream) {

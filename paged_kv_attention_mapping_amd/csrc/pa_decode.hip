@@ -128,6 +128,8 @@ struct RowArgs {
     float *ws_acc;             // [rows][hq][splits][D]
     float *ws_m;               // [rows][hq][splits]
     float *ws_l;
+    const _Float16 *k_scale;   // INT8 pools only: [slots][hkv] fp16 scales
+    const _Float16 *v_scale;
 };
 
 // This lane's slice of one query head, kept in the form the dot product wants:
@@ -351,6 +353,234 @@ __global__ __launch_bounds__(NW * kWave) void row_attn_split(RowArgs a, Rows row
     }
 }
 
+// INT8 pools (LLM inference interview notes (nano-vllm fork), Q3 part 2:
+// dequantization fused into the decode kernel, no float copy of the cache).
+// The same pass as row_attn_split over int8 codes with one fp16 scale per
+// (token, KV head): a lane loads 16 codes of K and 16 of V (LPT = D/16 lanes
+// per token) and the token's two scales.  Following the algebra the pages
+// suggest, the K scale multiplies the finished dot product instead of every
+// element, and the V scale is folded into the probability p (l keeps the
+// unscaled p):
+//     s_t = k_scale_t * sum_i q_i k_code_ti,   acc += (p_t * v_scale_t) * v_code_t.
+// Codes are widened with the byte-to-float conversion of their offset form
+// u = code + 128 (one XOR per 4 codes): sum q u - 128 sum q is the dot, and
+// the V accumulator subtracts 128 * sum of the folded p at the end.
+template <typename TQ, int D, int G, int NW, class Rows>
+__global__ __launch_bounds__(NW * kWave) void row_attn_int8(RowArgs a, Rows rows) {
+    constexpr int EPV = 16, LPT = D / EPV, TPW = kWave / LPT, TPR = NW * TPW * kUnroll;
+    constexpr int kT = NW * kWave;
+    static_assert(LPT >= 1 && LPT <= kWave && kWave % LPT == 0, "head_dim");
+    __shared__ int s_blk[kBlkIds];
+    __shared__ float s_acc[NW][G][D];
+    __shared__ float s_m[NW][G], s_l[NW][G];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1), w = tid >> 6;
+    const int tg = lane / LPT, c = lane % LPT;
+    const int hkv = a.hkv, hq = hkv * G;
+
+    const int64_t wg = blockIdx.x;
+    const int g = (int)(wg % hkv);
+    const int64_t rest = wg / hkv;
+    const int split = (int)(rest % a.num_splits);
+    const int row = rows.row_of((int)(rest / a.num_splits));
+    int seq, ctx;
+    rows.get(row, seq, ctx);
+    ctx = (int)min((int64_t)ctx, min((int64_t)a.bt_stride << a.block_shift,
+                                     (int64_t)a.num_splits * a.split_tokens));
+
+    TQ *out_row = reinterpret_cast<TQ *>(a.out) + ((int64_t)row * hq + (int64_t)g * G) * D;
+    const int t0 = split * a.split_tokens;
+    if (t0 >= ctx) {
+        if (split == 0)
+            for (int i = tid; i < G * D; i += kT) store_elem<TQ>(out_row + i, 0.f);
+        return;
+    }
+    const int t1 = min(t0 + a.split_tokens, ctx);
+    const int nsplit_row = (ctx + a.split_tokens - 1) / a.split_tokens;
+    const int shift = a.block_shift;
+    const int bmask = (1 << shift) - 1;
+    const int b0 = t0 >> shift;
+    {
+        const int32_t *bt = a.block_table + (int64_t)seq * a.bt_stride;
+        const int nb = ((t1 - 1) >> shift) - b0 + 1;
+        for (int i = tid; i < nb; i += kT) {
+            const int p = bt[b0 + i];
+            s_blk[i] = (p >= 0 && (int64_t)p < a.num_blocks) ? p : -1;
+        }
+    }
+    // this lane's 16 elements of each query head, as fp32, and their sum
+    float qv[G][EPV], qsum[G];
+    {
+        const TQ *qrow = reinterpret_cast<const TQ *>(a.q) + (int64_t)row * a.q_row_stride + (int64_t)g * G * D;
+        constexpr int QE = 16 / Elem<TQ>::bytes;
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+#pragma unroll
+            for (int h = 0; h < EPV / QE; ++h) unpack16<TQ>(ld16(qrow + j * D + c * EPV + h * QE), &qv[j][h * QE]);
+            float sq = 0.f;
+#pragma unroll
+            for (int e = 0; e < EPV; ++e) sq += qv[j][e];
+            qsum[j] = sq;
+        }
+    }
+    __syncthreads();
+
+    const int8_t *kp = reinterpret_cast<const int8_t *>(a.k_pool);
+    const int8_t *vp = reinterpret_cast<const int8_t *>(a.v_pool);
+    const int64_t head_off = (int64_t)g * D + c * EPV;
+    const int64_t slot_stride = (int64_t)hkv * D;
+
+    float m[G], l[G], ps[G], acc[G][EPV];
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+        m[j] = -INFINITY;
+        l[j] = 0.f;
+        ps[j] = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) acc[j][e] = 0.f;
+    }
+
+    // u_e = code_e + 128 as fp32 (byte e of the 16 after flipping each sign bit)
+    auto widen = [](const uint4 &x, float (&u)[EPV]) {
+        const uint32_t wd[4] = {x.x ^ 0x80808080u, x.y ^ 0x80808080u, x.z ^ 0x80808080u, x.w ^ 0x80808080u};
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int b = 0; b < 4; ++b) u[4 * i + b] = (float)((wd[i] >> (8 * b)) & 0xffu);
+    };
+    auto issue = [&](uint4 (&kr)[kUnroll], uint4 (&vr)[kUnroll], float (&ks)[kUnroll], float (&vs)[kUnroll],
+                     int (&blk)[kUnroll], int base) {
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int tok = base + (u * NW + w) * TPW + tg;
+            blk[u] = tok < t1 ? s_blk[(tok >> shift) - b0] : -1;
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int tok = base + (u * NW + w) * TPW + tg;
+            const int64_t slot = blk[u] >= 0 ? ((int64_t)blk[u] << shift) + (tok & bmask) : 0;
+            kr[u] = ld16_stream(kp + slot * slot_stride + head_off);
+            vr[u] = ld16_stream(vp + slot * slot_stride + head_off);
+            ks[u] = (float)a.k_scale[slot * hkv + g];
+            vs[u] = (float)a.v_scale[slot * hkv + g];
+        }
+    };
+    auto consume = [&](const uint4 (&kr)[kUnroll], const uint4 (&vr)[kUnroll], const float (&ks)[kUnroll],
+                       const float (&vs)[kUnroll], const int (&blk)[kUnroll]) {
+        float sc[kUnroll][G];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            float ku[EPV];
+            widen(kr[u], ku);
+#pragma unroll
+            for (int j = 0; j < G; ++j) {
+                float d0 = 0.f;
+#pragma unroll
+                for (int e = 0; e < EPV; ++e) d0 = fmaf(qv[j][e], ku[e], d0);
+                const float dot = group_sum<LPT>(fmaf(-128.f, qsum[j], d0));
+                sc[u][j] = blk[u] >= 0 ? dot * ks[u] * a.scale_log2 : -INFINITY;
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            float mx = m[j];
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) mx = fmaxf(mx, sc[u][j]);
+            const float m_use = (mx == -INFINITY) ? 0.f : mx;
+            const float alpha = exp2f(m[j] - m_use);
+            m[j] = mx;
+            float pl = 0.f, pv = 0.f;
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                const float p = exp2f(sc[u][j] - m_use);
+                pl += p;
+                sc[u][j] = blk[u] >= 0 ? p * vs[u] : 0.f;  // V scale folded into p
+                pv += sc[u][j];
+            }
+            l[j] = l[j] * alpha + pl;
+            ps[j] = ps[j] * alpha + pv;
+#pragma unroll
+            for (int e = 0; e < EPV; ++e) acc[j][e] *= alpha;
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            float vu[EPV];
+            widen(vr[u], vu);
+#pragma unroll
+            for (int j = 0; j < G; ++j)
+#pragma unroll
+                for (int e = 0; e < EPV; ++e) acc[j][e] = fmaf(sc[u][j], vu[e], acc[j][e]);
+        }
+    };
+    {
+        uint4 kA[kUnroll], vA[kUnroll], kB[kUnroll], vB[kUnroll];
+        float ksA[kUnroll], vsA[kUnroll], ksB[kUnroll], vsB[kUnroll];
+        int bA[kUnroll], bB[kUnroll];
+        issue(kA, vA, ksA, vsA, bA, t0);
+        for (int base = t0; base < t1; base += 2 * TPR) {
+            issue(kB, vB, ksB, vsB, bB, base + TPR);
+            consume(kA, vA, ksA, vsA, bA);
+            if (base + TPR >= t1) break;
+            issue(kA, vA, ksA, vsA, bA, base + 2 * TPR);
+            consume(kB, vB, ksB, vsB, bB);
+        }
+    }
+    // codes were offset by 128: remove 128 * (sum of folded p) from every element
+#pragma unroll
+    for (int j = 0; j < G; ++j)
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) acc[j][e] = fmaf(-128.f, ps[j], acc[j][e]);
+
+    // ---- combine the token groups of the wave, then the waves (as row_attn_split)
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+        float M = m[j];
+#pragma unroll
+        for (int sft = LPT; sft < kWave; sft <<= 1) M = fmaxf(M, __shfl_xor(M, sft));
+        const float f = (m[j] == -INFINITY) ? 0.f : exp2f(m[j] - M);
+        l[j] = cross_group_sum<LPT>(l[j] * f);
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) acc[j][e] = cross_group_sum<LPT>(acc[j][e] * f);
+        m[j] = M;
+    }
+    if (tg == 0) {
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+#pragma unroll
+            for (int e = 0; e < EPV; ++e) s_acc[w][j][c * EPV + e] = acc[j][e];
+            if (c == 0) {
+                s_m[w][j] = m[j];
+                s_l[w][j] = l[j];
+            }
+        }
+    }
+    __syncthreads();
+    for (int i = tid; i < G * D; i += kT) {
+        const int j = i / D, d = i - j * D;
+        float M = -INFINITY;
+#pragma unroll
+        for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, s_m[ww][j]);
+        float A = 0.f, L = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < NW; ++ww) {
+            const float f = (s_m[ww][j] == -INFINITY) ? 0.f : exp2f(s_m[ww][j] - M);
+            A += s_acc[ww][j][d] * f;
+            L += s_l[ww][j] * f;
+        }
+        if (nsplit_row == 1) {
+            store_elem<TQ>(out_row + i, L > 0.f ? A / L : 0.f);
+        } else {
+            const int64_t idx = ((int64_t)row * hq + g * G + j) * a.num_splits + split;
+            a.ws_acc[idx * D + d] = A;
+            if (d == 0) {
+                a.ws_m[idx] = M;
+                a.ws_l[idx] = L;
+            }
+        }
+    }
+}
+
 struct MergeArgs {
     int num_rows;
     int hq;
@@ -419,17 +649,21 @@ __global__ __launch_bounds__(kThreads) void row_attn_merge(MergeArgs a, Rows row
 }
 
 int tokens_per_round(int dtype, int d, int nw) {
-    const int epv = dtype == 0 ? 4 : 8;
+    const int epv = dtype == 0 ? 4 : (dtype == 1 ? 8 : 16);  // fp32, bf16, int8
     const int lpt = d / epv;
     return nw * (kWave / lpt) * kUnroll;
 }
 
-template <typename T, int D, int G, int NW, class Rows>
+template <typename T, int D, int G, int NW, class Rows, bool I8 = false>
 hipError_t run_rows(const RowArgs &a, const Rows &rows, hipStream_t stream) {
     const int64_t wgs = (int64_t)a.num_rows * a.num_splits * a.hkv;
     if (wgs == 0) return hipSuccess;
-    hipLaunchKernelGGL((row_attn_split<T, D, G, NW, Rows>), dim3((unsigned)wgs), dim3(NW * kWave), 0,
-                       stream, a, rows);
+    if constexpr (I8)
+        hipLaunchKernelGGL((row_attn_int8<T, D, G, NW, Rows>), dim3((unsigned)wgs), dim3(NW * kWave), 0,
+                           stream, a, rows);
+    else
+        hipLaunchKernelGGL((row_attn_split<T, D, G, NW, Rows>), dim3((unsigned)wgs), dim3(NW * kWave), 0,
+                           stream, a, rows);
     if (a.num_splits > 1) {
         MergeArgs m{a.num_rows, a.hkv * G, a.num_splits, a.split_tokens, a.bt_stride, a.block_shift,
                     a.ws_acc, a.ws_m, a.ws_l, a.out};
@@ -440,34 +674,36 @@ hipError_t run_rows(const RowArgs &a, const Rows &rows, hipStream_t stream) {
     return hipGetLastError();
 }
 
-template <typename T, int D, int G, class Rows>
+template <typename T, int D, int G, class Rows, bool I8 = false>
 hipError_t dispatch_waves(int waves, const RowArgs &a, const Rows &rows, hipStream_t s) {
     if constexpr (G <= 2) {  // wider workgroups only where the registers allow them
-        if (waves == 16) return run_rows<T, D, G, 16>(a, rows, s);
-        if (waves == 8) return run_rows<T, D, G, 8>(a, rows, s);
+        if (waves == 16) return run_rows<T, D, G, 16, Rows, I8>(a, rows, s);
+        if (waves == 8) return run_rows<T, D, G, 8, Rows, I8>(a, rows, s);
     }
-    if (waves == 4) return run_rows<T, D, G, 4>(a, rows, s);
+    if (waves == 4) return run_rows<T, D, G, 4, Rows, I8>(a, rows, s);
     return hipErrorInvalidValue;
 }
 
-template <typename T, int D, class Rows>
+template <typename T, int D, class Rows, bool I8 = false>
 hipError_t dispatch_group(int group, int waves, const RowArgs &a, const Rows &rows, hipStream_t s) {
     switch (group) {
-        case 1: return dispatch_waves<T, D, 1>(waves, a, rows, s);
-        case 2: return dispatch_waves<T, D, 2>(waves, a, rows, s);
-        case 4: return dispatch_waves<T, D, 4>(waves, a, rows, s);
-        case 8: return dispatch_waves<T, D, 8>(waves, a, rows, s);
+        case 1: return dispatch_waves<T, D, 1, Rows, I8>(waves, a, rows, s);
+        case 2: return dispatch_waves<T, D, 2, Rows, I8>(waves, a, rows, s);
+        case 4: return dispatch_waves<T, D, 4, Rows, I8>(waves, a, rows, s);
+        case 8:
+            if constexpr (!I8) return dispatch_waves<T, D, 8, Rows, I8>(waves, a, rows, s);
+            break;
     }
     return hipErrorInvalidValue;
 }
 
-template <typename T, class Rows>
+template <typename T, class Rows, bool I8 = false>
 hipError_t dispatch_dim(int d, int group, int waves, const RowArgs &a, const Rows &rows, hipStream_t s) {
     switch (d) {
-        case 32: return dispatch_group<T, 32>(group, waves, a, rows, s);
-        case 64: return dispatch_group<T, 64>(group, waves, a, rows, s);
-        case 128: return dispatch_group<T, 128>(group, waves, a, rows, s);
-        case 256: return dispatch_group<T, 256>(group, waves, a, rows, s);
+        case 32: return dispatch_group<T, 32, Rows, I8>(group, waves, a, rows, s);
+        case 64: return dispatch_group<T, 64, Rows, I8>(group, waves, a, rows, s);
+        case 128: return dispatch_group<T, 128, Rows, I8>(group, waves, a, rows, s);
+        case 256: return dispatch_group<T, 256, Rows, I8>(group, waves, a, rows, s);
     }
     return hipErrorInvalidValue;
 }
@@ -515,9 +751,14 @@ RowAttnPlan plan_row_attention(int num_rows, const PoolGeom &g, int group, int m
     // Wider workgroups stream one (row, KV head) faster, which shortens the
     // tail when context lengths are ragged; two per CU keep one streaming
     // while the other starts up or reduces.
-    int waves = group <= 2 ? 8 : 4;
+    // INT8 pools: 4 waves (the int8 kernel's per-lane state needs about 150
+    // registers; at 8 waves the compiler caps it at 128 and spills).
+    int waves = (group <= 2 && g.dtype != 2) ? 8 : 4;
 #ifdef PA_WAVES_OVERRIDE
     waves = PA_WAVES_OVERRIDE;
+#endif
+#ifdef PA_I8_WAVES
+    if (g.dtype == 2) waves = group <= 2 ? PA_I8_WAVES : 4;
 #endif
     RowAttnPlan p{num_rows, 1, 1, waves};
     if (num_rows <= 0 || max_keys <= 0) return p;
@@ -554,6 +795,21 @@ hipError_t launch_decode(const void *q, int64_t q_row_stride, int hq, const void
     const RowArgs a = make_args(q, q_row_stride, hq, k_pool, v_pool, g, block_table, bt_stride, plan,
                                 softmax_scale, out, workspace);
     return dispatch(g, hq / g.hkv, plan.waves, a, DecodeRows{context_lens, row_order}, stream);
+}
+
+hipError_t launch_decode_int8(const void *q, int64_t q_row_stride, int hq, int q_dtype, const void *k_pool,
+                              const void *v_pool, const void *k_scale, const void *v_scale, const PoolGeom &g,
+                              const int32_t *context_lens, const int32_t *block_table, int bt_stride,
+                              const RowAttnPlan &plan, float softmax_scale, const int32_t *row_order, void *out,
+                              void *workspace, hipStream_t stream) {
+    RowArgs a = make_args(q, q_row_stride, hq, k_pool, v_pool, g, block_table, bt_stride, plan, softmax_scale,
+                          out, workspace);
+    a.k_scale = reinterpret_cast<const _Float16 *>(k_scale);
+    a.v_scale = reinterpret_cast<const _Float16 *>(v_scale);
+    const DecodeRows rows{context_lens, row_order};
+    const int group = hq / g.hkv;
+    return q_dtype == 0 ? dispatch_dim<float, DecodeRows, true>(g.d, group, plan.waves, a, rows, stream)
+                        : dispatch_dim<bf16_t, DecodeRows, true>(g.d, group, plan.waves, a, rows, stream);
 }
 
 hipError_t launch_decode_order(const int32_t *context_lens, int num_rows, int32_t *row_order,

@@ -29,6 +29,10 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
     return u >> 16;
 }
 
+// One stored element as fp32 (exact).
+__device__ __forceinline__ float to_float(float x) { return x; }
+__device__ __forceinline__ float to_float(bf16_t x) { return bf16_lo(x.bits); }
+
 // Unpack one 16-byte vector into its elements as fp32.
 template <typename T> __device__ __forceinline__ void unpack16(const uint4 &v, float *f);
 template <> __device__ __forceinline__ void unpack16<float>(const uint4 &v, float *f) {

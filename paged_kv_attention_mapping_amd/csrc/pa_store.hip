@@ -8,6 +8,8 @@
 // wave moves 1 KiB of each per instruction; a token row of Hkv*d elements
 // (2 KiB at 8 heads x 128 x bf16) is 128 lanes.  When the rows or the
 // pointers are not 16-byte aligned a lane copies single elements instead.
+#include <type_traits>
+
 #include "pa_device.h"
 #include "pa_kernels.h"
 
@@ -77,7 +79,107 @@ __global__ __launch_bounds__(kStoreThreads) void gather_kv_vec16(
 
 inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
+// Quantizing store (LLM inference interview notes (nano-vllm fork), Q3 part
+// 1: quantization happens on write, fused into the store).  For each token t
+// with a valid slot and each KV head h, the head_dim values x of K (and of V)
+// become int8 codes with one scale:
+//   scale = max(max_i |x_i| / 127, 1e-8)              (fp32)
+//   code_i = trunc(x_i / scale + (x_i / scale >= 0 ? 0.5 : -0.5))
+// and the scale is stored as fp16 (round to nearest even).  The division is
+// IEEE fp32 (the compiler's default for HIP), so the codes are exactly those
+// of the same steps on a CPU.
+//
+// Mapping: a group of L lanes owns one head vector; each lane loads 16 bytes
+// of it (E = 8 bf16 or 4 fp32 values), the group reduces max |x| with xor
+// shuffles, then each lane writes its E codes and lane 0 the scale.  All lanes
+// run the shuffles; only loads and stores are guarded.
+template <typename SrcT, bool VEC>
+__global__ __launch_bounds__(kStoreThreads) void store_kv_int8(
+    const SrcT *__restrict__ k, int64_t k_stride, const SrcT *__restrict__ v, int64_t v_stride,
+    const int32_t *__restrict__ slot_mapping, int64_t num_vectors, int hkv, int d, int lanes,
+    int8_t *__restrict__ k_pool, int8_t *__restrict__ v_pool, _Float16 *__restrict__ k_scale,
+    _Float16 *__restrict__ v_scale, int64_t num_slots) {
+    constexpr int E = 16 / sizeof(SrcT);
+    const int64_t gid = (int64_t)blockIdx.x * kStoreThreads + threadIdx.x;
+    const int64_t vec = gid / lanes;  // t * hkv + h
+    const int li = (int)(gid - vec * lanes);
+    const int64_t t = vec / hkv;
+    const int h = (int)(vec - t * hkv);
+    int64_t slot = -1;
+    if (vec < num_vectors) slot = slot_mapping[t];
+    const bool ok = slot >= 0 && slot < num_slots;
+
+    auto quantize = [&](const SrcT *src, int8_t *dst_pool, _Float16 *dst_scale) {
+        float x[E];
+        if (ok) {
+            const SrcT *p = src + h * d + li * E;
+            if constexpr (VEC) {
+                unpack16<SrcT>(ld16(p), x);
+            } else {
+#pragma unroll
+                for (int e = 0; e < E; ++e) x[e] = to_float(p[e]);
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < E; ++e) x[e] = 0.f;
+        }
+        float amax = 0.f;
+#pragma unroll
+        for (int e = 0; e < E; ++e) amax = fmaxf(amax, fabsf(x[e]));
+        for (int o = lanes >> 1; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+        const float scale = fmaxf(amax / 127.0f, 1.0e-8f);
+        uint32_t packed[E / 4];
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const float qf = x[e] / scale;
+            const int code = (int)truncf(qf >= 0.f ? qf + 0.5f : qf - 0.5f);
+            if (e % 4 == 0) packed[e / 4] = 0;
+            packed[e / 4] |= ((uint32_t)code & 0xFFu) << (8 * (e % 4));
+        }
+        if (ok) {
+            int8_t *q = dst_pool + (slot * hkv + h) * d + li * E;
+            if constexpr (E == 8)
+                *reinterpret_cast<uint2 *>(q) = make_uint2(packed[0], packed[1]);
+            else
+                *reinterpret_cast<uint32_t *>(q) = packed[0];
+            if (li == 0) dst_scale[slot * hkv + h] = (_Float16)scale;
+        }
+    };
+    quantize(k + t * k_stride, k_pool, k_scale);
+    quantize(v + t * v_stride, v_pool, v_scale);
+}
+
 }  // namespace
+
+hipError_t launch_store_kv_int8(const void *k, int64_t k_row_stride, const void *v, int64_t v_row_stride,
+                                int src_dtype, const int32_t *slot_mapping, int num_tokens, void *k_pool,
+                                void *v_pool, void *k_scale, void *v_scale, const PoolGeom &g,
+                                hipStream_t stream) {
+    if (num_tokens == 0) return hipSuccess;
+    const int eb = src_dtype == 0 ? 4 : 2;
+    const int E = 16 / eb;
+    const int lanes = g.d / E;  // head_dim is a multiple of 8 and at most 512 (checked by the caller)
+    const int64_t vectors = (int64_t)num_tokens * g.hkv;
+    const int64_t threads = vectors * lanes;
+    const unsigned grid = (unsigned)((threads + kStoreThreads - 1) / kStoreThreads);
+    const int64_t num_slots = g.num_blocks << g.block_shift;
+    const bool vec = (k_row_stride * eb) % 16 == 0 && (v_row_stride * eb) % 16 == 0 && aligned16(k) &&
+                     aligned16(v);
+    auto go = [&](auto src_tag, auto vec_tag) {
+        using S = decltype(src_tag);
+        constexpr bool V = decltype(vec_tag)::value;
+        hipLaunchKernelGGL((store_kv_int8<S, V>), dim3(grid), dim3(kStoreThreads), 0, stream,
+                           (const S *)k, k_row_stride, (const S *)v, v_row_stride, slot_mapping, vectors,
+                           g.hkv, g.d, lanes, (int8_t *)k_pool, (int8_t *)v_pool, (_Float16 *)k_scale,
+                           (_Float16 *)v_scale, num_slots);
+    };
+    if (src_dtype == 0) {
+        if (vec) go(float{}, std::true_type{}); else go(float{}, std::false_type{});
+    } else {
+        if (vec) go(bf16_t{}, std::true_type{}); else go(bf16_t{}, std::false_type{});
+    }
+    return hipGetLastError();
+}
 
 hipError_t launch_store_kv(const void *k, int64_t k_row_stride, const void *v, int64_t v_row_stride,
                            const int32_t *slot_mapping, int num_tokens, void *k_pool, void *v_pool,

@@ -17,7 +17,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 def _declared_symbols():
     text = open(os.path.join(ROOT, "include", "pa.h")).read()
-    return set(re.findall(r"^\S.*?\b(pa_[a-z_]+)\s*\(", text, flags=re.M))
+    return set(re.findall(r"^\S.*?\b(pa_[a-z0-9_]+)\s*\(", text, flags=re.M))
 
 
 def test_header_declares_what_the_binding_expects():
@@ -28,13 +28,61 @@ def test_library_loads_and_exports_every_symbol():
     lib = pa.load()
     for name in _declared_symbols():
         assert hasattr(lib, name), name
-    assert lib.pa_abi_version() == 2
+    assert lib.pa_abi_version() == 3
     assert lib.pa_status_string(0) == b"ok"
     assert b"workspace" in lib.pa_status_string(5)
 
 
 def _pool(nb=4, bs=16, hkv=2, d=32, dtype=pa.PA_F32):
     return pa.PaPool(nb, bs, hkv, d, dtype)
+
+
+def test_int8_store_host_errors():
+    """pa_store_kv_int8 takes PA_INT8 pools only (and the bf16/fp32 calls
+    refuse them), bf16 or fp32 sources, head_dim a multiple of 8."""
+    lib = pa.load()
+    i8 = _pool(d=128, dtype=pa.PA_INT8)
+    dummy = ctypes.c_void_p(4096)
+    args = [dummy, 256, dummy, 256, pa.PA_BF16, dummy, 3, dummy, dummy, dummy, dummy, ctypes.byref(i8), None]
+    a = list(args); a[11] = ctypes.byref(_pool(d=128, dtype=pa.PA_BF16))
+    assert lib.pa_store_kv_int8(*a) == 3                       # pool not INT8
+    a = list(args); a[4] = pa.PA_INT8
+    assert lib.pa_store_kv_int8(*a) == 3                       # source must be bf16 / fp32
+    a = list(args); a[11] = ctypes.byref(_pool(d=36, dtype=pa.PA_INT8))
+    assert lib.pa_store_kv_int8(*a) == 4                       # head_dim % 8
+    a = list(args); a[6] = 0
+    assert lib.pa_store_kv_int8(*a) == 0                       # no tokens: no-op
+    a = list(args); a[9] = None
+    assert lib.pa_store_kv_int8(*a) == 1                       # scale pool missing
+    a = list(args); a[1] = 100
+    assert lib.pa_store_kv_int8(*a) == 2                       # row stride < Hkv * D
+    a = list(args); a[8] = ctypes.c_void_p(4100)
+    assert lib.pa_store_kv_int8(*a) == 4                       # code pool not 8-byte aligned
+    assert lib.pa_store_kv(dummy, 256, dummy, 256, dummy, 1, dummy, dummy, ctypes.byref(i8), None) == 3
+
+
+def test_int8_decode_host_errors_and_workspace():
+    """pa_decode_int8 takes PA_INT8 pools, q of bf16 / fp32, query groups of
+    1, 2 or 4; its workspace follows the same split plan as pa_decode."""
+    lib = pa.load()
+    dummy = ctypes.c_void_p(4096)
+    i8 = _pool(nb=64, bs=16, hkv=8, d=128, dtype=pa.PA_INT8)
+    def call(pool, hq=16, qd=pa.PA_BF16, n=4, scale=0.1, ws=None, wsb=0, max_ctx=100):
+        return lib.pa_decode_int8(dummy, hq * 128, hq, qd, dummy, dummy, dummy, dummy, ctypes.byref(pool),
+                                  dummy, dummy, 8, n, max_ctx, scale, None, dummy, ws, wsb, None)
+    assert call(_pool(nb=64, bs=16, hkv=8, d=128, dtype=pa.PA_BF16)) == 3   # pool not INT8
+    assert call(i8, qd=pa.PA_INT8) == 3                                      # q must be bf16 / fp32
+    assert call(i8, hq=64) == 4                                              # group 8 not built for INT8
+    assert call(i8, hq=12) == 2                                              # not a multiple of Hkv
+    assert call(i8, scale=0.0) == 2
+    assert call(i8, n=0) == 0
+    assert lib.pa_decode(dummy, 16 * 128, 16, dummy, dummy, ctypes.byref(i8), dummy, dummy, 8, 4, 100, 0.1,
+                         None, dummy, None, 0, None) == 3                    # bf16 decode refuses INT8 pools
+    # one long row splits: a workspace is required and sized like pa_decode's fp32 partials
+    need = lib.pa_decode_int8_workspace_bytes(1, 16, 1 << 16, ctypes.byref(i8))
+    assert need > 0 and need % (16 * (128 + 2) * 4) == 0
+    assert call(i8, n=1, max_ctx=1 << 16) == 5                             # split plan, no workspace given
+    assert lib.pa_decode_int8_workspace_bytes(256, 16, 2048, ctypes.byref(i8)) == 0
 
 
 def test_host_argument_errors_return_before_launch():
