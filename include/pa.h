@@ -139,7 +139,9 @@ pa_status pa_store_kv_int8(const void *k, int64_t k_row_stride,
  * finished dot product and the V scale is folded into the probability.
  *
  *   q, out        [num_seqs][num_q_heads][head_dim] of q_dtype (PA_BF16 or
- *                 PA_F32); q rows at q_row_stride elements, 16-byte aligned.
+ *                 PA_F32); q rows at q_row_stride elements, 16-byte aligned;
+ *                 bf16 q values must lie within fp16's range (|q| <= 65504;
+ *                 the K dot products run on fp16 pairs).
  *   k_pool,v_pool int8 code pools, 16-byte aligned; k_scale,v_scale fp16
  *                 scale pools (layout above); pool->dtype PA_INT8.
  *   everything else as pa_decode (context_lens, block_table, row_order,

@@ -27,6 +27,7 @@
 // The same kernel also serves as the vector-ALU prefill path: a prefill row is
 // one packed query token whose context is min(q_offset + i + 1, k_len) keys.
 #include <limits.h>
+#include <type_traits>
 #include <math.h>
 
 #include "pa_device.h"
@@ -362,9 +363,13 @@ __global__ __launch_bounds__(NW * kWave) void row_attn_split(RowArgs a, Rows row
 // element, and the V scale is folded into the probability p (l keeps the
 // unscaled p):
 //     s_t = k_scale_t * sum_i q_i k_code_ti,   acc += (p_t * v_scale_t) * v_code_t.
-// Codes are widened with the byte-to-float conversion of their offset form
-// u = code + 128 (one XOR per 4 codes): sum q u - 128 sum q is the dot, and
-// the V accumulator subtracts 128 * sum of the folded p at the end.
+// Codes are used in their offset form u = code + 128 (one XOR per 4 codes).
+// K, with bf16 queries: a byte permute turns two codes into the fp16 pair
+// (1024 + u0, 1024 + u1), exact integers, and v_dot2_f32_f16 takes them
+// against the queries converted to fp16 (exact for bf16 values inside
+// fp16's range); the dot is sum q (1152 + code) - 1152 sum q.  fp32 queries
+// use fp32 products of the widened u.  V: u widened to fp32, and the
+// accumulator subtracts 128 * sum of the folded p at the end.
 template <typename TQ, int D, int G, int NW, class Rows>
 __global__ __launch_bounds__(NW * kWave) void row_attn_int8(RowArgs a, Rows rows) {
     constexpr int EPV = 16, LPT = D / EPV, TPW = kWave / LPT, TPR = NW * TPW * kUnroll;
@@ -410,7 +415,11 @@ __global__ __launch_bounds__(NW * kWave) void row_attn_int8(RowArgs a, Rows rows
         }
     }
     // this lane's 16 elements of each query head, as fp32, and their sum
+    // (bf16 queries: as fp16 pairs for v_dot2_f32_f16, summed as fp16 values)
+    constexpr bool kF16Dot = std::is_same<TQ, bf16_t>::value;
+    typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
     float qv[G][EPV], qsum[G];
+    half2_t qh[G][EPV / 2];
     {
         const TQ *qrow = reinterpret_cast<const TQ *>(a.q) + (int64_t)row * a.q_row_stride + (int64_t)g * G * D;
         constexpr int QE = 16 / Elem<TQ>::bytes;
@@ -420,8 +429,15 @@ __global__ __launch_bounds__(NW * kWave) void row_attn_int8(RowArgs a, Rows rows
             for (int h = 0; h < EPV / QE; ++h) unpack16<TQ>(ld16(qrow + j * D + c * EPV + h * QE), &qv[j][h * QE]);
             float sq = 0.f;
 #pragma unroll
-            for (int e = 0; e < EPV; ++e) sq += qv[j][e];
+            for (int e = 0; e < EPV; ++e) {
+                if constexpr (kF16Dot) qv[j][e] = (float)(_Float16)qv[j][e];
+                sq += qv[j][e];
+            }
             qsum[j] = sq;
+            if constexpr (kF16Dot) {
+#pragma unroll
+                for (int e = 0; e < EPV; e += 2) qh[j][e / 2] = (half2_t){(_Float16)qv[j][e], (_Float16)qv[j][e + 1]};
+            }
         }
     }
     __syncthreads();
@@ -471,15 +487,35 @@ __global__ __launch_bounds__(NW * kWave) void row_attn_int8(RowArgs a, Rows rows
         float sc[kUnroll][G];
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
-            float ku[EPV];
-            widen(kr[u], ku);
+            if constexpr (kF16Dot) {
+                // code pairs as fp16 (1024 + code + 128): one byte permute per pair
+                const uint32_t wd[4] = {kr[u].x ^ 0x80808080u, kr[u].y ^ 0x80808080u, kr[u].z ^ 0x80808080u,
+                                        kr[u].w ^ 0x80808080u};
+                half2_t kp2[EPV / 2];
 #pragma unroll
-            for (int j = 0; j < G; ++j) {
-                float d0 = 0.f;
+                for (int i = 0; i < 4; ++i) {
+                    kp2[2 * i] = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0x64646464u, wd[i], 0x05010400u));
+                    kp2[2 * i + 1] = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0x64646464u, wd[i], 0x05030402u));
+                }
 #pragma unroll
-                for (int e = 0; e < EPV; ++e) d0 = fmaf(qv[j][e], ku[e], d0);
-                const float dot = group_sum<LPT>(fmaf(-128.f, qsum[j], d0));
-                sc[u][j] = blk[u] >= 0 ? dot * ks[u] * a.scale_log2 : -INFINITY;
+                for (int j = 0; j < G; ++j) {
+                    float d0 = 0.f;
+#pragma unroll
+                    for (int i = 0; i < EPV / 2; ++i) d0 = __builtin_amdgcn_fdot2(qh[j][i], kp2[i], d0, false);
+                    const float dot = group_sum<LPT>(fmaf(-1152.f, qsum[j], d0));
+                    sc[u][j] = blk[u] >= 0 ? dot * ks[u] * a.scale_log2 : -INFINITY;
+                }
+            } else {
+                float ku[EPV];
+                widen(kr[u], ku);
+#pragma unroll
+                for (int j = 0; j < G; ++j) {
+                    float d0 = 0.f;
+#pragma unroll
+                    for (int e = 0; e < EPV; ++e) d0 = fmaf(qv[j][e], ku[e], d0);
+                    const float dot = group_sum<LPT>(fmaf(-128.f, qsum[j], d0));
+                    sc[u][j] = blk[u] >= 0 ? dot * ks[u] * a.scale_log2 : -INFINITY;
+                }
             }
         }
 #pragma unroll
