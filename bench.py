@@ -18,6 +18,12 @@ pair over the prefill call's time).  Both come from HIP events recorded on
 the stream the kernels run on.  `roofline` is for the decode kernel (the
 dominant cost), `prefill.roofline` for the prefill kernel.  `cpu_baseline`
 times the fp64 CPU oracle on a bounded sample of the same decode workload.
+
+Outside the timed step, the INT8 KV cache is measured on the same shapes:
+`int8_decode` times pa_decode_int8 over INT8 pools quantized from four of
+the decode layers (bytes: every visible row's int8 codes and fp16 scale,
+K and V, once per KV head), and `int8_store` times pa_store_kv_int8 of the
+4096-token prompt.
 """
 from __future__ import annotations
 
@@ -43,6 +49,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--layers", type=int, default=28)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-int8", action="store_true", help="skip the INT8 KV-cache measurements")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="also run one plain 1 GiB device copy (HBM counter calibration)")
     return p.parse_args()
@@ -170,6 +177,9 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
 
+    int8 = None if args.no_int8 else int8_measure(pa, W, lay, pf, k_pools, v_pools, qs, ctx_d, bt_d, order_d,
+                                                  pf_kn, pf_vn, pf_slots, dec_call_ms, max(args.steps, 2))
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(lay, k_pools[0], v_pools[0], qs[0])
@@ -221,7 +231,84 @@ def main():
         "cpu_baseline": cpu,
         "host_wall_s": round(wall, 3),
     }
+    if int8 is not None:
+        result.update(int8)
     print(json.dumps(result), flush=True)
+
+
+def int8_measure(pa, W, lay, pf, k_pools, v_pools, qs, ctx_d, bt_d, order_d, pf_kn, pf_vn, pf_slots,
+                 bf16_call_ms, reps, layers=4):
+    """INT8 KV cache on the decode and prefill shapes (not part of the step)."""
+    import torch
+    dev = "cuda"
+    stream = torch.cuda.current_stream()
+    nb, bs, hkv, d, hq = lay.num_blocks, lay.block_size, lay.num_kv_heads, lay.head_dim, lay.num_q_heads
+    layers = min(layers, len(k_pools))
+    all_slots = torch.arange(nb * bs, dtype=torch.int32, device=dev)
+    pools = []
+    for i in range(layers):
+        kq = torch.empty((nb, bs, hkv, d), dtype=torch.int8, device=dev)
+        vq = torch.empty_like(kq)
+        ks = torch.empty((nb, bs, hkv), dtype=torch.float16, device=dev)
+        vs = torch.empty_like(ks)
+        pa.pa_store_kv_int8(k_pools[i].view(nb * bs, hkv, d), v_pools[i].view(nb * bs, hkv, d), all_slots,
+                            kq, vq, ks, vs)
+        pools.append((kq, vq, ks, vs))
+    out = torch.empty((lay.num_seqs, hq, d), dtype=torch.bfloat16, device=dev)
+    wsb = pa.pa_decode_int8_workspace_bytes(lay.num_seqs, hq, lay.max_context_len, pools[0][0], pools[0][2])
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+    tokens = int(lay.context_lens.astype(np.int64).sum()) * hkv
+    i8_bytes = tokens * (d + 2) * 2
+
+    def dec(i):
+        pa.pa_decode_int8(qs[i], *pools[i], ctx_d, bt_d, lay.max_context_len, lay.scale, out=out, workspace=ws,
+                          row_order=order_d)
+
+    for i in range(layers):
+        dec(i)
+    torch.cuda.synchronize()
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(layers)]
+          for _ in range(reps)]
+    for r in range(reps):
+        for i in range(layers):
+            ev[r][i][0].record(stream)
+            dec(i)
+            ev[r][i][1].record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for row in ev for a, b in row]))
+    gbps = i8_bytes / (ms * 1e-3) / 1e9
+
+    # quantizing store of the 4096-token prompt into an INT8 pool of the prefill layout
+    kq = torch.empty((pf.num_blocks, pf.block_size, pf.num_kv_heads, pf.head_dim), dtype=torch.int8, device=dev)
+    vq = torch.empty_like(kq)
+    ks = torch.empty((pf.num_blocks, pf.block_size, pf.num_kv_heads), dtype=torch.float16, device=dev)
+    vs = torch.empty_like(ks)
+    for _ in range(2):
+        pa.pa_store_kv_int8(pf_kn, pf_vn, pf_slots, kq, vq, ks, vs)
+    torch.cuda.synchronize()
+    sev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in sev:
+        a.record(stream)
+        pa.pa_store_kv_int8(pf_kn, pf_vn, pf_slots, kq, vq, ks, vs)
+        b.record(stream)
+    torch.cuda.synchronize()
+    st_ms = float(np.mean([a.elapsed_time(b) for a, b in sev]))
+    st_bytes = pf.total_q * pf.num_kv_heads * (pf.head_dim * 2 + pf.head_dim + 2) * 2  # read bf16, write int8+scale
+    return {
+        "int8_decode": {
+            "value": round(gbps, 2), "unit": "GB/s",
+            "workload": f"decode 256 seqs ctx U[100,2048], int8 codes + fp16 scales, {layers} layer pools",
+            "avg_launch_us": round(ms * 1e3, 2), "bytes_per_launch": i8_bytes,
+            "speedup_vs_bf16_decode": round(bf16_call_ms / ms, 3),
+            "roofline": {"bound": "hbm", "achieved": round(gbps, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                         "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": measured_traffic("decode_int8")},
+        },
+        "int8_store": {
+            "workload": "pa_store_kv_int8 of 4096 tokens x 8 KV heads x 128 (bf16 in, int8 + fp16 scale out)",
+            "avg_launch_us": round(st_ms * 1e3, 2), "bytes_per_launch": st_bytes,
+            "achieved_gbps": round(st_bytes / (st_ms * 1e-3) / 1e9, 2),
+        },
+    }
 
 
 def measured_traffic(which):
