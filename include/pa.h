@@ -160,6 +160,27 @@ pa_status pa_decode_int8(const void *q, int64_t q_row_stride, int32_t num_q_head
                          void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * pa_prefill_varlen_int8 -- pa_prefill_varlen over INT8 pools, with the
+ * dequantization fused into the attention instead of first gathering the
+ * referenced K/V into a float tensor (the slow path the same answer, part 3,
+ * describes for prefill).  Same arguments, semantics and errors as
+ * pa_prefill_varlen, plus q_dtype (PA_BF16 / PA_F32, also out's type) and the
+ * fp16 scale pools; INT8 pools as for pa_decode_int8 (query groups 1, 2, 4).
+ * Each packed query token is one row of the INT8 decode pass over its
+ * visible keys (vector ALU, not the matrix cores).
+ */
+size_t pa_prefill_int8_workspace_bytes(int32_t num_seqs, int32_t total_q, int32_t num_q_heads,
+                                       int32_t max_seqlen_k, const pa_pool *pool /* host */);
+pa_status pa_prefill_varlen_int8(const void *q, int64_t q_row_stride, int32_t num_q_heads, int32_t q_dtype,
+                                 const void *k_pool, const void *v_pool,
+                                 const void *k_scale, const void *v_scale, const pa_pool *pool /* host */,
+                                 const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k,
+                                 const int32_t *q_offsets, const int32_t *block_table,
+                                 int32_t block_table_stride, int32_t num_seqs, int32_t total_q,
+                                 int32_t max_seqlen_q, int32_t max_seqlen_k, float softmax_scale,
+                                 void *out, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * pa_prefill_varlen -- causal attention for a packed variable-length batch
  * over the paged cache (nano-vllm deep dive, Step 4, flash_attn_varlen_func
  * with cu_seqlens_q / cu_seqlens_k / block_table, causal; Step 5,

@@ -21,6 +21,7 @@ from ._lib import (  # noqa: F401
     pa_decode_workspace_bytes,
     pa_gather_kv,
     pa_prefill_varlen,
+    pa_prefill_varlen_int8,
     pa_prefill_workspace_bytes,
     pa_store_kv,
     pa_store_kv_int8,

@@ -27,7 +27,8 @@ _STATUS = {
 # Every symbol include/pa.h declares.
 EXPORTS = (
     "pa_store_kv", "pa_store_kv_int8", "pa_prefill_varlen", "pa_decode", "pa_decode_int8",
-    "pa_decode_int8_workspace_bytes", "pa_decode_order",
+    "pa_decode_int8_workspace_bytes", "pa_prefill_varlen_int8", "pa_prefill_int8_workspace_bytes",
+    "pa_decode_order",
     "pa_prefill_workspace_bytes",
     "pa_decode_workspace_bytes", "pa_gather_kv", "pa_validate_prefill_metadata",
     "pa_validate_decode_metadata", "pa_status_string", "pa_abi_version",
@@ -68,6 +69,10 @@ def load() -> ctypes.CDLL:
     lib.pa_decode_int8.argtypes = [p, i64, i32, i32, p, p, p, p, pool, p, p, i32, i32, i32, f32, p, p, p, sz, p]
     lib.pa_decode_int8_workspace_bytes.argtypes = [i32, i32, i32, pool]
     lib.pa_decode_int8_workspace_bytes.restype = sz
+    lib.pa_prefill_varlen_int8.argtypes = [p, i64, i32, i32, p, p, p, p, pool, p, p, p, p, i32, i32, i32, i32,
+                                           i32, f32, p, p, sz, p]
+    lib.pa_prefill_int8_workspace_bytes.argtypes = [i32, i32, i32, i32, pool]
+    lib.pa_prefill_int8_workspace_bytes.restype = sz
     lib.pa_decode_order.argtypes = [p, i32, p, p]
     lib.pa_prefill_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, pool]
     lib.pa_prefill_workspace_bytes.restype = sz
@@ -79,7 +84,8 @@ def load() -> ctypes.CDLL:
     lib.pa_status_string.argtypes = [i32]
     lib.pa_status_string.restype = ctypes.c_char_p
     lib.pa_abi_version.restype = ctypes.c_int
-    for fn in ("pa_store_kv", "pa_store_kv_int8", "pa_prefill_varlen", "pa_decode", "pa_decode_int8", "pa_decode_order", "pa_gather_kv",
+    for fn in ("pa_store_kv", "pa_store_kv_int8", "pa_prefill_varlen", "pa_prefill_varlen_int8", "pa_decode",
+               "pa_decode_int8", "pa_decode_order", "pa_gather_kv",
                "pa_validate_prefill_metadata", "pa_validate_decode_metadata"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
@@ -298,6 +304,36 @@ def pa_decode_int8(q, k_pool, v_pool, k_scale, v_scale, context_lens, block_tabl
         _ptr(v_scale), ctypes.byref(pool), _ptr(context_lens), _ptr(block_table), block_table.shape[1], b,
         int(max_context_len), float(softmax_scale), _ptr(row_order), _ptr(out), _ptr(workspace), wbytes,
         _stream()))
+    return out
+
+
+def pa_prefill_varlen_int8(q, k_pool, v_pool, k_scale, v_scale, cu_seqlens_q, cu_seqlens_k, q_offsets,
+                           block_table, max_seqlen_q, max_seqlen_k, softmax_scale, out=None, workspace=None):
+    """pa_prefill_varlen over INT8 pools (int8 codes, fp16 scales); q/out bf16 or fp32."""
+    lib = load()
+    _dev(q, k_pool, v_pool, k_scale, v_scale)
+    pool = pool_desc_int8(k_pool, k_scale)
+    if v_pool.shape != k_pool.shape or v_pool.dtype != torch.int8 or not v_pool.is_contiguous():
+        raise ValueError("v_pool must match k_pool")
+    if v_scale.shape != k_scale.shape or v_scale.dtype != torch.float16 or not v_scale.is_contiguous():
+        raise ValueError("v_scale must match k_scale")
+    total_q, hq, d = q.shape
+    if d != pool.head_dim:
+        raise ValueError("q must match the pools' head_dim")
+    cu_q, cu_k = _i32(cu_seqlens_q, "cu_seqlens_q"), _i32(cu_seqlens_k, "cu_seqlens_k")
+    q_offsets, block_table = _i32(q_offsets, "q_offsets"), _i32(block_table, "block_table")
+    num_seqs = cu_q.numel() - 1
+    if out is None:
+        out = torch.empty((total_q, hq, d), dtype=q.dtype, device=q.device)
+    elif not out.is_contiguous() or out.shape != (total_q, hq, d) or out.dtype != q.dtype:
+        raise ValueError("out must be contiguous [total_q, Hq, D] of q's dtype")
+    nbytes = int(lib.pa_prefill_int8_workspace_bytes(num_seqs, total_q, hq, int(max_seqlen_k), ctypes.byref(pool)))
+    workspace, wbytes = _workspace(nbytes, workspace, q.device)
+    _check("pa_prefill_varlen_int8", lib.pa_prefill_varlen_int8(
+        _ptr(q), _row_stride(q, hq * d, "q"), hq, _dtype_code(q), _ptr(k_pool), _ptr(v_pool), _ptr(k_scale),
+        _ptr(v_scale), ctypes.byref(pool), _ptr(cu_q), _ptr(cu_k), _ptr(q_offsets), _ptr(block_table),
+        block_table.shape[1], num_seqs, total_q, int(max_seqlen_q), int(max_seqlen_k), float(softmax_scale),
+        _ptr(out), _ptr(workspace), wbytes, _stream()))
     return out
 
 

@@ -265,6 +265,47 @@ pa_status pa_decode_int8(const void *q, int64_t q_row_stride, int32_t num_q_head
                                            row_order, out, workspace, (hipStream_t)stream));
 }
 
+size_t pa_prefill_int8_workspace_bytes(int32_t num_seqs, int32_t total_q, int32_t num_q_heads,
+                                       int32_t max_seqlen_k, const pa_pool *pool) {
+    pa::PoolGeom g;
+    if (check_decode_int8_shape(pool, num_q_heads, PA_BF16, &g) != PA_OK) return 0;
+    if (num_seqs <= 0 || total_q <= 0 || max_seqlen_k <= 0) return 0;
+    const pa::RowAttnPlan plan = pa::plan_row_attention(total_q, g, num_q_heads / g.hkv, max_seqlen_k);
+    return pa::row_attention_workspace_bytes(plan, num_q_heads, g.d);
+}
+
+pa_status pa_prefill_varlen_int8(const void *q, int64_t q_row_stride, int32_t num_q_heads, int32_t q_dtype,
+                                 const void *k_pool, const void *v_pool, const void *k_scale, const void *v_scale,
+                                 const pa_pool *pool, const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k,
+                                 const int32_t *q_offsets, const int32_t *block_table, int32_t block_table_stride,
+                                 int32_t num_seqs, int32_t total_q, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                 float softmax_scale, void *out, void *workspace, size_t workspace_bytes,
+                                 void *stream) {
+    (void)max_seqlen_q;
+    pa::PoolGeom g;
+    pa_status st = check_decode_int8_shape(pool, num_q_heads, q_dtype, &g);
+    if (st != PA_OK) return st;
+    if (num_seqs < 0 || total_q < 0 || max_seqlen_q < 0 || max_seqlen_k < 0) return PA_ERR_BAD_SHAPE;
+    if (!scale_ok(softmax_scale)) return PA_ERR_BAD_SHAPE;
+    if (num_seqs == 0 || total_q == 0) return PA_OK;
+    if (!q || !k_pool || !v_pool || !k_scale || !v_scale || !cu_seqlens_q || !cu_seqlens_k || !q_offsets ||
+        !block_table || !out)
+        return PA_ERR_NULL_ARG;
+    if (block_table_stride <= 0) return PA_ERR_BAD_SHAPE;
+    if (q_row_stride < (int64_t)num_q_heads * g.d) return PA_ERR_BAD_SHAPE;
+    const int eb = elem_bytes(q_dtype);
+    if (!aligned16(q) || (q_row_stride * eb) % 16 || !aligned16(k_pool) || !aligned16(v_pool) ||
+        ((reinterpret_cast<uintptr_t>(k_scale) | reinterpret_cast<uintptr_t>(v_scale)) & 1))
+        return PA_ERR_UNSUPPORTED;
+    const pa::RowAttnPlan plan = pa::plan_row_attention(total_q, g, num_q_heads / g.hkv, max_seqlen_k);
+    const size_t need = pa::row_attention_workspace_bytes(plan, num_q_heads, g.d);
+    if (need && (!workspace || workspace_bytes < need)) return PA_ERR_WORKSPACE;
+    return from_hip(pa::launch_prefill_rows_int8(q, q_row_stride, num_q_heads, q_dtype, k_pool, v_pool, k_scale,
+                                                 v_scale, g, cu_seqlens_q, cu_seqlens_k, q_offsets, block_table,
+                                                 block_table_stride, num_seqs, plan, softmax_scale, out, workspace,
+                                                 (hipStream_t)stream));
+}
+
 pa_status pa_decode_order(const int32_t *context_lens, int32_t num_seqs, int32_t *row_order, void *stream) {
     if (num_seqs < 0) return PA_ERR_BAD_SHAPE;
     if (num_seqs == 0) return PA_OK;

@@ -867,4 +867,22 @@ hipError_t launch_prefill_rows(const void *q, int64_t q_row_stride, int hq, cons
                     PrefillRows{cu_seqlens_q, cu_seqlens_k, q_offsets, num_seqs}, stream);
 }
 
+// Prefill over INT8 pools, one packed query token per row (the decode pass
+// above with the INT8 dequantization fused in; no float copy of the cache).
+hipError_t launch_prefill_rows_int8(const void *q, int64_t q_row_stride, int hq, int q_dtype, const void *k_pool,
+                                    const void *v_pool, const void *k_scale, const void *v_scale,
+                                    const PoolGeom &g, const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k,
+                                    const int32_t *q_offsets, const int32_t *block_table, int bt_stride,
+                                    int num_seqs, const RowAttnPlan &plan, float softmax_scale, void *out,
+                                    void *workspace, hipStream_t stream) {
+    RowArgs a = make_args(q, q_row_stride, hq, k_pool, v_pool, g, block_table, bt_stride, plan, softmax_scale,
+                          out, workspace);
+    a.k_scale = reinterpret_cast<const _Float16 *>(k_scale);
+    a.v_scale = reinterpret_cast<const _Float16 *>(v_scale);
+    const PrefillRows rows{cu_seqlens_q, cu_seqlens_k, q_offsets, num_seqs};
+    const int group = hq / g.hkv;
+    return q_dtype == 0 ? dispatch_dim<float, PrefillRows, true>(g.d, group, plan.waves, a, rows, stream)
+                        : dispatch_dim<bf16_t, PrefillRows, true>(g.d, group, plan.waves, a, rows, stream);
+}
+
 }  // namespace pa

@@ -63,6 +63,14 @@ hipError_t launch_decode_int8(const void *q, int64_t q_row_stride, int hq, int q
                               const RowAttnPlan &plan, float softmax_scale, const int32_t *row_order, void *out,
                               void *workspace, hipStream_t stream);
 
+// Prefill over INT8 pools, one packed query token per row.
+hipError_t launch_prefill_rows_int8(const void *q, int64_t q_row_stride, int hq, int q_dtype, const void *k_pool,
+                                    const void *v_pool, const void *k_scale, const void *v_scale,
+                                    const PoolGeom &g, const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k,
+                                    const int32_t *q_offsets, const int32_t *block_table, int bt_stride,
+                                    int num_seqs, const RowAttnPlan &plan, float softmax_scale, void *out,
+                                    void *workspace, hipStream_t stream);
+
 // Longest-context-first permutation of decode rows (one workgroup).
 constexpr int kDecodeOrderMax = 2048;
 hipError_t launch_decode_order(const int32_t *context_lens, int num_rows, int32_t *row_order,

@@ -85,6 +85,22 @@ def test_int8_decode_host_errors_and_workspace():
     assert lib.pa_decode_int8_workspace_bytes(256, 16, 2048, ctypes.byref(i8)) == 0
 
 
+def test_int8_prefill_host_errors():
+    lib = pa.load()
+    dummy = ctypes.c_void_p(4096)
+    i8 = _pool(nb=64, bs=16, hkv=8, d=128, dtype=pa.PA_INT8)
+    def call(pool, hq=16, qd=pa.PA_BF16, n=2, tq=10, scale=0.1):
+        return lib.pa_prefill_varlen_int8(dummy, hq * 128, hq, qd, dummy, dummy, dummy, dummy, ctypes.byref(pool),
+                                          dummy, dummy, dummy, dummy, 8, n, tq, 5, 5, scale, dummy, None, 0, None)
+    assert call(_pool(nb=64, bs=16, hkv=8, d=128, dtype=pa.PA_BF16)) == 3
+    assert call(i8, qd=7) == 3
+    assert call(i8, hq=64) == 4
+    assert call(i8, scale=-1.0) == 2
+    assert call(i8, n=0) == 0 and call(i8, tq=0) == 0
+    assert lib.pa_prefill_varlen(dummy, 16 * 128, 16, dummy, dummy, ctypes.byref(i8), dummy, dummy, dummy, dummy,
+                                 8, 2, 10, 5, 5, 0.1, dummy, None, 0, None) == 3
+
+
 def test_host_argument_errors_return_before_launch():
     lib = pa.load()
     pool = _pool()

@@ -253,3 +253,96 @@ def test_decode_int8_c5b_sampled():
     err = max_abs_err(out[torch.as_tensor(seqs, device="cuda")], ref)
     say(f"  max-abs {err:.3e}")
     assert err <= tol("bf16")
+
+
+# ---------------------------------------------------------------- prefill
+
+PREFILL_CASES = {
+    "c2_8x32": lambda: W.c2_varlen(32),
+    "c2_8x128": lambda: W.c2_varlen(128),
+    "c3_prefix": W.c3_prefix,
+    "c1_prefill_f32_d32": lambda: W.c1_tiny()[0],
+    "ragged_g4_d64_bs8": lambda: W.make_prefill("i8_ragged", 901, [1, 67, 0, 130, 5], [0, 13, 9, 0, 250], 8, 2, 64,
+                                                8, "bf16"),
+    "ragged_g1_d256_f32": lambda: W.make_prefill("i8_ragged2", 902, [33, 4, 90], [7, 0, 100], 4, 4, 256, 16,
+                                                 "f32"),
+}
+
+
+@pytest.mark.parametrize("name", list(PREFILL_CASES))
+def test_prefill_int8_against_oracle(name):
+    case = PREFILL_CASES[name]()
+    nb, bs, hkv, d = case.empty_pools()[0].shape
+    say(f"[int8 prefill] {name}")
+    host = int8_pools(nb, bs, hkv, d)
+    dev = dev_pools(*host)
+    for k, v, s in ((case.k_cached, case.v_cached, case.slot_cached), (case.k_new, case.v_new, case.slot_new)):
+        if len(s):
+            pa.pa_store_kv_int8(to_dev(k), to_dev(v), to_dev(s), *dev)
+            Q.store_kv(k, v, s, *host)
+    offs = np.asarray(case.q_offsets, np.int32)
+    out = pa.pa_prefill_varlen_int8(to_dev(case.q), *dev, to_dev(case.cu_seqlens_q), to_dev(case.cu_seqlens_k),
+                                    to_dev(offs), to_dev(case.block_table), case.max_seqlen_q, case.max_seqlen_k,
+                                    case.scale)
+    torch.cuda.synchronize()
+    assert_pools_equal(dev, host)
+    ref = Q.prefill(case.q, *host, case.cu_seqlens_q, case.cu_seqlens_k, offs, case.block_table, case.scale)
+    err = max_abs_err(out, ref)
+    say(f"  max-abs {err:.3e}")
+    assert err <= tol(case.dtype)
+
+
+def test_prefill_int8_suffix_equals_rows_of_full_prefill():
+    """C3's 44-token suffixes over their cached 256-token blocks equal (to
+    the bf16 tolerance: the two launches split the rows' keys differently)
+    rows 256..299 of a full 300-token INT8 prefill over the same pools, and
+    both match the oracle."""
+    case = W.c3_prefix()
+    nb, bs, hkv, d = case.empty_pools()[0].shape
+    host = int8_pools(nb, bs, hkv, d)
+    dev = dev_pools(*host)
+    for k, v, s in ((case.k_cached, case.v_cached, case.slot_cached), (case.k_new, case.v_new, case.slot_new)):
+        pa.pa_store_kv_int8(to_dev(k), to_dev(v), to_dev(s), *dev)
+        Q.store_kv(k, v, s, *host)
+    offs = np.asarray(case.q_offsets, np.int32)
+    suffix = pa.pa_prefill_varlen_int8(to_dev(case.q), *dev, to_dev(case.cu_seqlens_q), to_dev(case.cu_seqlens_k),
+                                       to_dev(offs), to_dev(case.block_table), 44, 300, case.scale)
+    rng = np.random.default_rng(3)
+    q_full = W.normal(rng, (600, case.num_q_heads, d), "bf16")
+    q_full[256:300] = case.q[:44]
+    q_full[556:600] = case.q[44:]
+    full = pa.pa_prefill_varlen_int8(to_dev(q_full), *dev, to_dev(np.array([0, 300, 600], np.int32)),
+                                     to_dev(case.cu_seqlens_k), to_dev(np.zeros(2, np.int32)),
+                                     to_dev(case.block_table), 300, 300, case.scale)
+    torch.cuda.synchronize()
+    rows = torch.as_tensor(np.r_[256:300, 556:600], device="cuda")
+    ref = Q.prefill(case.q, *host, case.cu_seqlens_q, case.cu_seqlens_k, offs, case.block_table, case.scale)
+    assert max_abs_err(suffix, ref) <= tol("bf16")
+    assert max_abs_err(full[rows], ref) <= tol("bf16")
+
+
+def test_prefill_int8_c5a_mixed_sampled_rows():
+    """C5a-ii (8192 tokens over ~13 sequences, a resumed chunk first), INT8
+    pools, rows sampled across every sequence."""
+    case = W.c5a_mixed()
+    nb, bs, hkv, d = case.empty_pools()[0].shape
+    say(f"[int8 prefill] c5a mixed {case.total_q} tokens")
+    host = int8_pools(nb, bs, hkv, d)
+    dev = dev_pools(*host)
+    for k, v, s in ((case.k_cached, case.v_cached, case.slot_cached), (case.k_new, case.v_new, case.slot_new)):
+        if len(s):
+            pa.pa_store_kv_int8(to_dev(k), to_dev(v), to_dev(s), *dev)
+            Q.store_kv(k, v, s, *host)
+    offs = np.asarray(case.q_offsets, np.int32)
+    out = pa.pa_prefill_varlen_int8(to_dev(case.q), *dev, to_dev(case.cu_seqlens_q), to_dev(case.cu_seqlens_k),
+                                    to_dev(offs), to_dev(case.block_table), case.max_seqlen_q, case.max_seqlen_k,
+                                    case.scale)
+    torch.cuda.synchronize()
+    cu = np.asarray(case.cu_seqlens_q)
+    rows = np.unique(np.concatenate([cu[:-1], cu[1:] - 1, np.linspace(0, case.total_q - 1, 40).astype(np.int64)]))
+    rows = rows[(rows >= 0) & (rows < case.total_q)].astype(np.int32)
+    ref = Q.prefill(case.q, *host, case.cu_seqlens_q, case.cu_seqlens_k, offs, case.block_table, case.scale,
+                    rows=rows)
+    err = max_abs_err(out[torch.as_tensor(rows, device="cuda").long()], ref)
+    say(f"  max-abs {err:.3e} over {len(rows)} rows")
+    assert err <= tol("bf16")
