@@ -270,6 +270,8 @@ size_t pa_prefill_int8_workspace_bytes(int32_t num_seqs, int32_t total_q, int32_
     pa::PoolGeom g;
     if (check_decode_int8_shape(pool, num_q_heads, PA_BF16, &g) != PA_OK) return 0;
     if (num_seqs <= 0 || total_q <= 0 || max_seqlen_k <= 0) return 0;
+    // the row path's split partials (the MFMA path with bf16 queries needs none;
+    // an fp32-query call takes the row path, so the size covers it)
     const pa::RowAttnPlan plan = pa::plan_row_attention(total_q, g, num_q_heads / g.hkv, max_seqlen_k);
     return pa::row_attention_workspace_bytes(plan, num_q_heads, g.d);
 }
@@ -297,7 +299,14 @@ pa_status pa_prefill_varlen_int8(const void *q, int64_t q_row_stride, int32_t nu
     if (!aligned16(q) || (q_row_stride * eb) % 16 || !aligned16(k_pool) || !aligned16(v_pool) ||
         ((reinterpret_cast<uintptr_t>(k_scale) | reinterpret_cast<uintptr_t>(v_scale)) & 1))
         return PA_ERR_UNSUPPORTED;
-    const pa::RowAttnPlan plan = pa::plan_row_attention(total_q, g, num_q_heads / g.hkv, max_seqlen_k);
+    const int group = num_q_heads / g.hkv;
+    if (q_dtype == PA_BF16 && pa::prefill_mfma_int8_supported(g, group) && aligned16(out) &&
+        !((reinterpret_cast<uintptr_t>(k_scale) | reinterpret_cast<uintptr_t>(v_scale)) & 3))
+        return from_hip(pa::launch_prefill_mfma_int8(q, q_row_stride, num_q_heads, k_pool, v_pool, k_scale, v_scale,
+                                                     g, cu_seqlens_q, cu_seqlens_k, q_offsets, block_table,
+                                                     block_table_stride, num_seqs, max_seqlen_q, softmax_scale, out,
+                                                     (hipStream_t)stream));
+    const pa::RowAttnPlan plan = pa::plan_row_attention(total_q, g, group, max_seqlen_k);
     const size_t need = pa::row_attention_workspace_bytes(plan, num_q_heads, g.d);
     if (need && (!workspace || workspace_bytes < need)) return PA_ERR_WORKSPACE;
     return from_hip(pa::launch_prefill_rows_int8(q, q_row_stride, num_q_heads, q_dtype, k_pool, v_pool, k_scale,

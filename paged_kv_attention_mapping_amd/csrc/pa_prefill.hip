@@ -90,6 +90,18 @@ struct Pf {
     static constexpr int RPI = 64 / CPR;               // rows per wave-wide 16-byte load
     static constexpr int LPW = kRowsPerWave / RPI;     // 16-byte loads per lane per step (K or V)
     static constexpr int MERGE = DT * 16 + 2;          // floats per lane handed between key halves
+    // INT8 pools: one bf16 step buffer, an int8 staging step (D bytes per row)
+    // and the rows' scale words
+    static constexpr int DIM = D;
+    static constexpr int CPR8 = D / 16;                // 16-byte chunks per int8 row
+    static constexpr int STAGEB = kStep * D;           // bytes of one int8 step (K or V)
+    static constexpr int RPI8 = 64 / CPR8;             // int8 rows per wave-wide 16-byte load
+    static constexpr int LPW8 = kRowsPerWave / RPI8;   // such loads per lane per step (K or V)
+    static constexpr int CONV = kStep * CPR8 / kPfThreads;  // int8 chunks each thread converts (K or V)
+    static constexpr int SCLB = kStep * 4;             // bytes of one step's scale words (K or V)
+    static_assert(LPW8 * RPI8 == kRowsPerWave && CONV * kPfThreads == kStep * CPR8, "int8 row split");
+    static_assert(kStep == 128 && kPfWaves >= 4, "scale words: waves 0..3 fetch 64 rows each");
+    static_assert(4 * MERGE * 64 * 4 <= 2 * STEPB + 2 * STAGEB, "merge area fits in the INT8 layout");
     static_assert(LPW * RPI == kRowsPerWave && LPW >= 1, "row split");
     static_assert((4 * RPI) % CPR == 0, "V swizzle independent of the load index");
     static_assert(4 * MERGE * 64 * 4 <= 4 * STEPB, "merge area fits in the K/V buffers");
@@ -113,6 +125,8 @@ struct PfArgs {
     int pairs_per_seq;
     float scale_log2;
     uint16_t *out;
+    const uint16_t *k_scale;   // INT8 pools: fp16 scales [slots][hkv]
+    const uint16_t *v_scale;
 };
 
 __device__ __forceinline__ int swap_bits_2_3(int i) {
@@ -183,6 +197,13 @@ __device__ __forceinline__ void global_lds16(const void *src, uint32_t lds_base)
                  : "v"(src), "s"(lds_base)
                  : "memory", "m0");
 }
+// 4 bytes per lane, lane i writing lds_base + 4 i.
+__device__ __forceinline__ void global_lds4(const void *src, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+                 :
+                 : "v"(src), "s"(lds_base)
+                 : "memory", "m0");
+}
 #pragma clang diagnostic pop
 
 // Direct HBM/L2 -> LDS loads of this wave's 16 rows of one step (keys
@@ -240,6 +261,101 @@ __device__ __forceinline__ void load_wave_rows(const PfArgs &a, int kb_step, int
                      __builtin_amdgcn_readfirstlane(lds_addr(dk) + blk_i * 1024));
         global_lds16(a.v_pool + eoff + v_slot<C::CPR>(r, sl) * 8,
                      __builtin_amdgcn_readfirstlane(lds_addr(dv) + blk_i * 1024));
+    }
+}
+
+// INT8 pools (LLM inference interview notes (nano-vllm fork), Q3: K/V stored
+// as int8 codes with one fp16 scale per (token, KV head)).  Direct loads of
+// this wave's 16 code rows of one step into the int8 staging buffers dk / dv
+// (row-major, D bytes a row), rows resolved as in load_wave_rows; and, from
+// waves 0..3, one 4-byte scale word per step row (K for waves 0, 1, V for 2,
+// 3): the word holding the fp16 scales of heads g & ~1 and g | 1 (hkv is
+// even, so it is 4-byte aligned).
+template <class C>
+__device__ __forceinline__ void load_wave_rows_i8(const PfArgs &a, int kb_step, int kmax, int shift, int bmask,
+                                                  int win0, int blk0, int g, int w, int lane, const int *s_blk,
+                                                  unsigned char *dk, unsigned char *dv, unsigned char *dsk,
+                                                  unsigned char *dsv) {
+    const int64_t row_bytes = (int64_t)a.hkv * C::DIM;  // bytes of one pool slot
+    const int64_t head = (int64_t)g * C::DIM;
+    const unsigned char *kp = reinterpret_cast<const unsigned char *>(a.k_pool);
+    const unsigned char *vp = reinterpret_cast<const unsigned char *>(a.v_pool);
+    auto slot_of = [&](int key) -> int64_t {
+        const int p = key <= kmax ? s_blk[(key >> shift) - win0] : -1;
+        return p >= 0 ? ((int64_t)p << shift) + (key & bmask) : (blk0 >= 0 ? ((int64_t)blk0 << shift) : 0);
+    };
+    if (w < 4) {
+        const int r = (w & 1) * 64 + lane;
+        const uint16_t *sp = w < 2 ? a.k_scale : a.v_scale;
+        global_lds4(sp + slot_of(kb_step + r) * a.hkv + (g & ~1),
+                    __builtin_amdgcn_readfirstlane(lds_addr(w < 2 ? dsk : dsv) + (w & 1) * 256));
+    }
+    if (kb_step + kBN * (w / (kPfWaves / 2)) > kmax) return;
+    const int row0 = __builtin_amdgcn_readfirstlane(kb_step + kRowsPerWave * w);
+    if (shift >= 4 && row0 + kRowsPerWave - 1 <= kmax) {
+        const int p = __builtin_amdgcn_readfirstlane(s_blk[(row0 >> shift) - win0]);
+        if (p >= 0) {
+            const int64_t sbase = (((int64_t)p << shift) + (row0 & bmask)) * row_bytes + head;
+            const i32x4 rk = raw_rsrc(kp + sbase, (uint32_t)(kRowsPerWave * row_bytes));
+            const i32x4 rv = raw_rsrc(vp + sbase, (uint32_t)(kRowsPerWave * row_bytes));
+            const uint32_t off = (uint32_t)((lane / C::CPR8) * row_bytes + (lane % C::CPR8) * 16);
+            const uint32_t lk = __builtin_amdgcn_readfirstlane(lds_addr(dk) + w * C::LPW8 * 1024);
+            const uint32_t lv = __builtin_amdgcn_readfirstlane(lds_addr(dv) + w * C::LPW8 * 1024);
+#pragma unroll
+            for (int u = 0; u < C::LPW8; ++u) {
+                const int soff = __builtin_amdgcn_readfirstlane((int)(u * C::RPI8 * row_bytes));
+                buffer_lds16(rk, off, soff, lk + u * 1024);
+                buffer_lds16(rv, off, soff, lv + u * 1024);
+            }
+            return;
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < C::LPW8; ++u) {
+        const int blk_i = w * C::LPW8 + u;  // 1 KiB block of the staging step
+        const int q = blk_i * 64 + lane;
+        const int r = q / C::CPR8, c8 = q % C::CPR8;
+        const int64_t eoff = slot_of(kb_step + r) * row_bytes + head + c8 * 16;
+        global_lds16(kp + eoff, __builtin_amdgcn_readfirstlane(lds_addr(dk) + blk_i * 1024));
+        global_lds16(vp + eoff, __builtin_amdgcn_readfirstlane(lds_addr(dv) + blk_i * 1024));
+    }
+}
+
+// Dequantize one staged INT8 step into the bf16 step buffer: code * scale,
+// exact in fp32, rounded once to bf16 (nearest even), written in the same
+// swizzled layout the direct bf16 loads produce (K rows XOR r, V rows XOR 4r).
+// Codes are widened in their +128 offset form: (u - 128) s = fma(u, s, -128 s).
+template <class C>
+__device__ __forceinline__ void convert_step_i8(const unsigned char *k8, const unsigned char *v8,
+                                                const uint32_t *sk, const uint32_t *sv, int g, unsigned char *kt,
+                                                unsigned char *vt, int tid) {
+    typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+#pragma unroll
+    for (int t = 0; t < C::CONV; ++t) {
+        const int cid = tid + kPfThreads * t;
+        const int r = cid / C::CPR8, c8 = cid % C::CPR8;
+#pragma unroll
+        for (int kv = 0; kv < 2; ++kv) {
+            const uint4 codes = *reinterpret_cast<const uint4 *>((kv ? v8 : k8) + r * C::DIM + c8 * 16);
+            const uint32_t word = (kv ? sv : sk)[r];
+            const uint16_t bits = (uint16_t)((g & 1) ? (word >> 16) : (word & 0xffffu));
+            const float sc = (float)__builtin_bit_cast(_Float16, bits);
+            const float nsc = -128.f * sc;
+            const uint32_t wd[4] = {codes.x ^ 0x80808080u, codes.y ^ 0x80808080u, codes.z ^ 0x80808080u,
+                                    codes.w ^ 0x80808080u};
+            f32x8 lo, hi;
+#pragma unroll
+            for (int b = 0; b < 8; ++b) {
+                lo[b] = fmaf((float)((wd[b / 4] >> (8 * (b % 4))) & 0xffu), sc, nsc);
+                hi[b] = fmaf((float)((wd[2 + b / 4] >> (8 * (b % 4))) & 0xffu), sc, nsc);
+            }
+            const int c0 = 2 * c8;
+            const int s0 = kv ? v_slot<C::CPR>(r, c0) : k_slot<C::CPR>(r, c0);
+            const int s1 = kv ? v_slot<C::CPR>(r, c0 + 1) : k_slot<C::CPR>(r, c0 + 1);
+            unsigned char *tile = kv ? vt : kt;
+            *reinterpret_cast<bf16x8_t *>(tile + r * C::ROWB + s0 * 16) = __builtin_convertvector(lo, bf16x8_t);
+            *reinterpret_cast<bf16x8_t *>(tile + r * C::ROWB + s1 * 16) = __builtin_convertvector(hi, bf16x8_t);
+        }
     }
 }
 
@@ -482,14 +598,26 @@ __device__ __forceinline__ void load_and_attend(const PfArgs &a, bool load, int 
     if (tile) attend_tile<C>(cur, cur, kofs, vofs, qf, st, need_mask, thr, c);
 }
 
-template <int D, int NH>
+template <int D, int NH, bool I8>
 __global__ __launch_bounds__(kPfThreads, 1) void prefill_mfma_kernel(PfArgs a) {
     using C = Pf<D, NH>;
-    // [K, V][buffer][step rows]: every buffer and block offset of an LDS read
-    // is an immediate.  After the key loop the same memory carries the second
-    // key half's partial results to the first.
-    __shared__ __attribute__((aligned(1024))) unsigned char s_kv[2][2][C::STEPB];
+    // [K, V][buffer][step rows] bf16 step buffers: every buffer and block
+    // offset of an LDS read is an immediate.  bf16 pools: two buffers, the
+    // next step loading while this one is computed.  INT8 pools: one bf16
+    // buffer, then the int8 staging step (K, V) and its scale words: the next
+    // step's codes load while this one is computed, and are dequantized into
+    // the buffer between two barriers.  After the key loop the same memory
+    // carries the second key half's partial results to the first.
+    constexpr int NB = I8 ? 1 : 2;
+    constexpr int MEMB = I8 ? 2 * C::STEPB + 2 * C::STAGEB + 2 * C::SCLB : 4 * C::STEPB;
+    __shared__ __attribute__((aligned(1024))) unsigned char s_mem[MEMB];
     __shared__ int s_blk[kBlkWin];
+    auto kbuf = [&](int b) { return s_mem + b * C::STEPB; };
+    auto vbuf = [&](int b) { return s_mem + (NB + b) * C::STEPB; };
+    unsigned char *const s_k8 = s_mem + 2 * C::STEPB;  // INT8 only (past the end otherwise: never used)
+    unsigned char *const s_v8 = s_k8 + C::STAGEB;
+    uint32_t *const s_sk = reinterpret_cast<uint32_t *>(s_v8 + C::STAGEB);
+    uint32_t *const s_sv = s_sk + kStep;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = tid >> 6;
@@ -540,7 +668,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_mfma_kernel(PfArgs a) {
 #pragma unroll
         for (int dt = 0; dt < C::DT; ++dt) {
             const int chunk = 4 * dt + 2 * (grp & 1) + ((li & 3) >> 1);
-            vofs[dt] = 2 * C::STEPB + kh * C::TILEB + row * C::ROWB + v_slot<C::CPR>(row, chunk) * 16 + 8 * (li & 1);
+            vofs[dt] = NB * C::STEPB + kh * C::TILEB + row * C::ROWB + v_slot<C::CPR>(row, chunk) * 16 + 8 * (li & 1);
         }
     }
     // byte offsets, inside the pool, of this lane's 16-byte pieces of the
@@ -554,7 +682,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_mfma_kernel(PfArgs a) {
     for (int u = 0; u < C::LPW; ++u)
         koff[u] = (uint32_t)((lane / C::CPR) * kv_row * 2 +
                              k_slot<C::CPR>(C::RPI * u + lane / C::CPR, lane % C::CPR) * 16);
-    float *merge = reinterpret_cast<float *>(&s_kv[0][0][0]) + wl * (C::MERGE * 64);
+    float *merge = reinterpret_cast<float *>(s_mem) + wl * (C::MERGE * 64);
 
     for (int it = 0; it < 2; ++it) {
         const int tile = it == 0 ? T - 1 - pair : pair;
@@ -613,9 +741,17 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_mfma_kernel(PfArgs a) {
         stage_ids(0);
         __syncthreads();
         const int blk0 = s_blk[0];  // physical block of key 0 (finite stand-in for masked rows)
-        load_wave_rows<C>(a, 0, kmax_wg, shift, bmask, win0, blk0, kv_row, kv_head, koff, voff, w, lane, s_blk,
-                          s_kv[0][0], s_kv[1][0]);
-        __builtin_amdgcn_s_waitcnt(0);
+        if constexpr (I8) {
+            load_wave_rows_i8<C>(a, 0, kmax_wg, shift, bmask, win0, blk0, g, w, lane, s_blk, s_k8, s_v8,
+                                 reinterpret_cast<unsigned char *>(s_sk), reinterpret_cast<unsigned char *>(s_sv));
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            convert_step_i8<C>(s_k8, s_v8, s_sk, s_sv, g, kbuf(0), vbuf(0), tid);
+        } else {
+            load_wave_rows<C>(a, 0, kmax_wg, shift, bmask, win0, blk0, kv_row, kv_head, koff, voff, w, lane, s_blk,
+                              kbuf(0), vbuf(0));
+            __builtin_amdgcn_s_waitcnt(0);
+        }
         __syncthreads();
 
         // one step j in buffer BUF (compile-time): issue the loads of step
@@ -630,15 +766,38 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_mfma_kernel(PfArgs a) {
                 __syncthreads();
             }
             const int kb = j * kStep + kh * kBN;
-            load_and_attend<C>(a, load, kb1, kmax_wg, shift, bmask, win0, blk0, kv_row, kv_head, koff, voff, w, lane,
-                               s_blk, s_kv[0][BUF ^ 1], s_kv[1][BUF ^ 1], wave_active && kb <= kmax_w, s_kv[0][BUF],
-                               kofs, vofs, qf, sm, kb + kBN - 1 > kfull_w, lim_me - kb - 8 * hf, c);
-            __builtin_amdgcn_s_waitcnt(0);  // this wave's direct loads of step j+1 have landed
-            __syncthreads();
+            if constexpr (I8) {
+                // codes of step j+1 load into the staging step while step j is
+                // computed; after the barrier they are dequantized into the
+                // (now free) buffer
+                if (load)
+                    load_wave_rows_i8<C>(a, kb1, kmax_wg, shift, bmask, win0, blk0, g, w, lane, s_blk, s_k8, s_v8,
+                                         reinterpret_cast<unsigned char *>(s_sk),
+                                         reinterpret_cast<unsigned char *>(s_sv));
+                if (wave_active && kb <= kmax_w)
+                    attend_tile<C>(kbuf(0), kbuf(0), kofs, vofs, qf, sm, kb + kBN - 1 > kfull_w, lim_me - kb - 8 * hf,
+                                   c);
+                __builtin_amdgcn_s_waitcnt(0);
+                __syncthreads();
+                if (load) {
+                    convert_step_i8<C>(s_k8, s_v8, s_sk, s_sv, g, kbuf(0), vbuf(0), tid);
+                    __syncthreads();
+                }
+            } else {
+                load_and_attend<C>(a, load, kb1, kmax_wg, shift, bmask, win0, blk0, kv_row, kv_head, koff, voff, w,
+                                   lane, s_blk, kbuf(BUF ^ 1), vbuf(BUF ^ 1), wave_active && kb <= kmax_w, kbuf(BUF),
+                                   kofs, vofs, qf, sm, kb + kBN - 1 > kfull_w, lim_me - kb - 8 * hf, c);
+                __builtin_amdgcn_s_waitcnt(0);  // this wave's direct loads of step j+1 have landed
+                __syncthreads();
+            }
         };
-        for (int j = 0; j < nsteps; j += 2) {
-            step(j, std::integral_constant<int, 0>{});
-            if (j + 1 < nsteps) step(j + 1, std::integral_constant<int, 1>{});
+        if constexpr (I8) {
+            for (int j = 0; j < nsteps; ++j) step(j, std::integral_constant<int, 0>{});
+        } else {
+            for (int j = 0; j < nsteps; j += 2) {
+                step(j, std::integral_constant<int, 0>{});
+                if (j + 1 < nsteps) step(j + 1, std::integral_constant<int, 1>{});
+            }
         }
 
         // ---- the second key half hands (O, m, l) to the first through LDS
@@ -680,7 +839,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_mfma_kernel(PfArgs a) {
     }
 }
 
-template <int D, int NH>
+template <int D, int NH, bool I8>
 hipError_t run(const PfArgs &a, int num_seqs, int max_seqlen_q, hipStream_t stream) {
     using C = Pf<D, NH>;
     PfArgs b = a;
@@ -689,17 +848,17 @@ hipError_t run(const PfArgs &a, int num_seqs, int max_seqlen_q, hipStream_t stre
     b.head_groups = a.group / NH;
     const int64_t wgs = (int64_t)num_seqs * b.pairs_per_seq * b.head_groups * a.hkv;
     if (wgs == 0) return hipSuccess;
-    hipLaunchKernelGGL((prefill_mfma_kernel<D, NH>), dim3((unsigned)wgs), dim3(kPfThreads), 0, stream, b);
+    hipLaunchKernelGGL((prefill_mfma_kernel<D, NH, I8>), dim3((unsigned)wgs), dim3(kPfThreads), 0, stream, b);
     return hipGetLastError();
 }
 
-template <int D>
+template <int D, bool I8 = false>
 hipError_t dispatch_nh(const PfArgs &a, int num_seqs, int max_seqlen_q, hipStream_t stream) {
     switch (a.group) {
-        case 1: return run<D, 1>(a, num_seqs, max_seqlen_q, stream);
-        case 2: return run<D, 2>(a, num_seqs, max_seqlen_q, stream);
-        case 4: return run<D, 4>(a, num_seqs, max_seqlen_q, stream);
-        case 8: return run<D, 4>(a, num_seqs, max_seqlen_q, stream);
+        case 1: return run<D, 1, I8>(a, num_seqs, max_seqlen_q, stream);
+        case 2: return run<D, 2, I8>(a, num_seqs, max_seqlen_q, stream);
+        case 4: return run<D, 4, I8>(a, num_seqs, max_seqlen_q, stream);
+        case 8: return run<D, 4, I8>(a, num_seqs, max_seqlen_q, stream);
     }
     return hipErrorInvalidValue;
 }
@@ -739,6 +898,42 @@ hipError_t launch_prefill_mfma(const void *q, int64_t q_row_stride, int hq, cons
     if (max_seqlen_q <= 0) return hipSuccess;
     return g.d == 128 ? dispatch_nh<128>(a, num_seqs, max_seqlen_q, stream)
                       : dispatch_nh<64>(a, num_seqs, max_seqlen_q, stream);
+}
+
+bool prefill_mfma_int8_supported(const PoolGeom &g, int group) {
+    // INT8 pools with bf16 queries: the scale words are 4-byte pairs of heads
+    // (even hkv); 16 pool rows span < 2^31 bytes
+    return g.dtype == 2 && (g.d == 64 || g.d == 128) && g.block_size >= 4 && g.hkv % 2 == 0 &&
+           (group == 1 || group == 2 || group == 4) && (int64_t)g.hkv * g.d * kRowsPerWave < ((int64_t)1 << 31);
+}
+
+hipError_t launch_prefill_mfma_int8(const void *q, int64_t q_row_stride, int hq, const void *k_pool,
+                                    const void *v_pool, const void *k_scale, const void *v_scale, const PoolGeom &g,
+                                    const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k,
+                                    const int32_t *q_offsets, const int32_t *block_table, int bt_stride,
+                                    int num_seqs, int max_seqlen_q, float softmax_scale, void *out,
+                                    hipStream_t stream) {
+    PfArgs a{};
+    a.q = reinterpret_cast<const uint16_t *>(q);
+    a.q_row_stride = q_row_stride;
+    a.k_pool = reinterpret_cast<const uint16_t *>(k_pool);
+    a.v_pool = reinterpret_cast<const uint16_t *>(v_pool);
+    a.k_scale = reinterpret_cast<const uint16_t *>(k_scale);
+    a.v_scale = reinterpret_cast<const uint16_t *>(v_scale);
+    a.num_blocks = g.num_blocks;
+    a.block_shift = g.block_shift;
+    a.hkv = g.hkv;
+    a.group = hq / g.hkv;
+    a.block_table = block_table;
+    a.bt_stride = bt_stride;
+    a.cu_q = cu_seqlens_q;
+    a.cu_k = cu_seqlens_k;
+    a.q_off = q_offsets;
+    a.scale_log2 = softmax_scale * kLog2eF;
+    a.out = reinterpret_cast<uint16_t *>(out);
+    if (max_seqlen_q <= 0) return hipSuccess;
+    return g.d == 128 ? dispatch_nh<128, true>(a, num_seqs, max_seqlen_q, stream)
+                      : dispatch_nh<64, true>(a, num_seqs, max_seqlen_q, stream);
 }
 
 }  // namespace pa

@@ -346,3 +346,25 @@ def test_prefill_int8_c5a_mixed_sampled_rows():
     err = max_abs_err(out[torch.as_tensor(rows, device="cuda").long()], ref)
     say(f"  max-abs {err:.3e} over {len(rows)} rows")
     assert err <= tol("bf16")
+
+
+def test_prefill_int8_c5a_4096_sampled_rows():
+    """C5a-i (1 x 4096, block 16) over INT8 pools on the query-tiled MFMA path."""
+    case = W.c5a_long()
+    nb, bs, hkv, d = case.empty_pools()[0].shape
+    say("[int8 prefill] c5a 1x4096")
+    host = int8_pools(nb, bs, hkv, d)
+    dev = dev_pools(*host)
+    pa.pa_store_kv_int8(to_dev(case.k_new), to_dev(case.v_new), to_dev(case.slot_new), *dev)
+    Q.store_kv(case.k_new, case.v_new, case.slot_new, *host)
+    offs = np.zeros(1, np.int32)
+    out = pa.pa_prefill_varlen_int8(to_dev(case.q), *dev, to_dev(case.cu_seqlens_q), to_dev(case.cu_seqlens_k),
+                                    to_dev(offs), to_dev(case.block_table), 4096, 4096, case.scale)
+    torch.cuda.synchronize()
+    rows = np.unique(np.r_[0, 1, 31, 32, 63, 64, 127, 128, 1000, 2047, 2048, 4000, 4095,
+                           np.random.default_rng(9).integers(0, 4096, 24)]).astype(np.int32)
+    ref = Q.prefill(case.q, *host, case.cu_seqlens_q, case.cu_seqlens_k, offs, case.block_table, case.scale,
+                    rows=rows)
+    err = max_abs_err(out[torch.as_tensor(rows, device="cuda").long()], ref)
+    say(f"  max-abs {err:.3e}")
+    assert err <= tol("bf16")
