@@ -22,8 +22,8 @@ times the fp64 CPU oracle on a bounded sample of the same decode workload.
 Outside the timed step, the INT8 KV cache is measured on the same shapes:
 `int8_decode` times pa_decode_int8 over INT8 pools quantized from four of
 the decode layers (bytes: every visible row's int8 codes and fp16 scale,
-K and V, once per KV head), and `int8_store` times pa_store_kv_int8 of the
-4096-token prompt.
+K and V, once per KV head), `int8_store` times pa_store_kv_int8 of the
+4096-token prompt and `int8_prefill` pa_prefill_varlen_int8 over it.
 """
 from __future__ import annotations
 
@@ -178,7 +178,8 @@ def main():
         torch.cuda.synchronize()
 
     int8 = None if args.no_int8 else int8_measure(pa, W, lay, pf, k_pools, v_pools, qs, ctx_d, bt_d, order_d,
-                                                  pf_kn, pf_vn, pf_slots, dec_call_ms, max(args.steps, 2))
+                                                  pf_kn, pf_vn, pf_slots, dec_call_ms, max(args.steps, 2),
+                                                  (pf_q, pf_cuq, pf_cuk, pf_off, pf_bt, pf_flops, pf_call_ms))
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -237,7 +238,7 @@ def main():
 
 
 def int8_measure(pa, W, lay, pf, k_pools, v_pools, qs, ctx_d, bt_d, order_d, pf_kn, pf_vn, pf_slots,
-                 bf16_call_ms, reps, layers=4):
+                 bf16_call_ms, reps, pf_args, layers=4):
     """INT8 KV cache on the decode and prefill shapes (not part of the step)."""
     import torch
     dev = "cuda"
@@ -294,6 +295,26 @@ def int8_measure(pa, W, lay, pf, k_pools, v_pools, qs, ctx_d, bt_d, order_d, pf_
     torch.cuda.synchronize()
     st_ms = float(np.mean([a.elapsed_time(b) for a, b in sev]))
     st_bytes = pf.total_q * pf.num_kv_heads * (pf.head_dim * 2 + pf.head_dim + 2) * 2  # read bf16, write int8+scale
+
+    # prefill over the INT8 pool just filled (1 x 4096 causal, block 16)
+    pf_q, pf_cuq, pf_cuk, pf_off, pf_bt, pf_flops, pf_bf16_ms = pf_args
+    pf_out = torch.empty_like(pf_q)
+
+    def pre():
+        pa.pa_prefill_varlen_int8(pf_q, kq, vq, ks, vs, pf_cuq, pf_cuk, pf_off, pf_bt, pf.max_seqlen_q,
+                                  pf.max_seqlen_k, pf.scale, out=pf_out)
+
+    for _ in range(2):
+        pre()
+    torch.cuda.synchronize()
+    pev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in pev:
+        a.record(stream)
+        pre()
+        b.record(stream)
+    torch.cuda.synchronize()
+    pf_ms = float(np.mean([a.elapsed_time(b) for a, b in pev]))
+    pf_tflops = pf_flops / (pf_ms * 1e-3) / 1e12
     return {
         "int8_decode": {
             "value": round(gbps, 2), "unit": "GB/s",
@@ -302,6 +323,14 @@ def int8_measure(pa, W, lay, pf, k_pools, v_pools, qs, ctx_d, bt_d, order_d, pf_
             "speedup_vs_bf16_decode": round(bf16_call_ms / ms, 3),
             "roofline": {"bound": "hbm", "achieved": round(gbps, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                          "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": measured_traffic("decode_int8")},
+        },
+        "int8_prefill": {
+            "value": round(pf_tflops, 2), "unit": "TFLOP/s",
+            "workload": "prefill 1x4096 causal over INT8 pools (block 16), bf16 queries",
+            "avg_launch_us": round(pf_ms * 1e3, 2), "flops_per_launch": pf_flops,
+            "time_vs_bf16_prefill": round(pf_ms / pf_bf16_ms, 3),
+            "roofline": {"bound": "mfma", "achieved": round(pf_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(pf_tflops / MFMA_BF16_PEAK_TFLOPS, 4)},
         },
         "int8_store": {
             "workload": "pa_store_kv_int8 of 4096 tokens x 8 KV heads x 128 (bf16 in, int8 + fp16 scale out)",
