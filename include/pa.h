@@ -181,6 +181,29 @@ pa_status pa_prefill_varlen_int8(const void *q, int64_t q_row_stride, int32_t nu
                                  void *out, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * pa_copy_blocks -- copy-on-write of shared, mutable last blocks (vLLM/SGLang
+ * interview labs, section 4, the follow-up on a native block-table fork: the
+ * parent and child share block ids; an append that would land in a shared,
+ * still-mutable last block first gives the child a new block holding a copy
+ * of the valid KV; full immutable blocks are never copied).  For each pair i,
+ * slots 0 .. num_valid[i]-1 of physical block src_blocks[i] are copied bit for
+ * bit to the same slots of block dst_blocks[i], in the K and V pools and, for
+ * PA_INT8 pools, in the scale pools; every other slot is left unchanged.
+ *
+ *   k_pool, v_pool   the layer's pools (any dtype); k_scale, v_scale the fp16
+ *                    scale pools of a PA_INT8 layer (ignored otherwise).
+ *   src_blocks, dst_blocks, num_valid   device int32 [num_pairs].
+ * Preconditions: destination blocks are distinct and none is a source in the
+ * same call.  Pairs with ids outside [0, num_blocks) or num_valid outside
+ * [1, block_size] are skipped.  Errors: the pool checks of pa_store_kv /
+ * pa_store_kv_int8; num_pairs == 0 is a no-op.
+ */
+pa_status pa_copy_blocks(void *k_pool, void *v_pool, void *k_scale, void *v_scale,
+                         const pa_pool *pool /* host */, const int32_t *src_blocks,
+                         const int32_t *dst_blocks, const int32_t *num_valid, int32_t num_pairs,
+                         void *stream);
+
+/*
  * pa_prefill_varlen -- causal attention for a packed variable-length batch
  * over the paged cache (nano-vllm deep dive, Step 4, flash_attn_varlen_func
  * with cu_seqlens_q / cu_seqlens_k / block_table, causal; Step 5,

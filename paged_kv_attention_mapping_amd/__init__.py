@@ -14,6 +14,7 @@ from ._lib import (  # noqa: F401
     PaError,
     PaPool,
     load,
+    pa_copy_blocks,
     pa_decode,
     pa_decode_int8,
     pa_decode_int8_workspace_bytes,

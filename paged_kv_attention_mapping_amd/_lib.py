@@ -28,7 +28,7 @@ _STATUS = {
 EXPORTS = (
     "pa_store_kv", "pa_store_kv_int8", "pa_prefill_varlen", "pa_decode", "pa_decode_int8",
     "pa_decode_int8_workspace_bytes", "pa_prefill_varlen_int8", "pa_prefill_int8_workspace_bytes",
-    "pa_decode_order",
+    "pa_decode_order", "pa_copy_blocks",
     "pa_prefill_workspace_bytes",
     "pa_decode_workspace_bytes", "pa_gather_kv", "pa_validate_prefill_metadata",
     "pa_validate_decode_metadata", "pa_status_string", "pa_abi_version",
@@ -63,6 +63,7 @@ def load() -> ctypes.CDLL:
     pool = ctypes.POINTER(PaPool)
     lib.pa_store_kv.argtypes = [p, i64, p, i64, p, i32, p, p, pool, p]
     lib.pa_store_kv_int8.argtypes = [p, i64, p, i64, i32, p, i32, p, p, p, p, pool, p]
+    lib.pa_copy_blocks.argtypes = [p, p, p, p, pool, p, p, p, i32, p]
     lib.pa_prefill_varlen.argtypes = [p, i64, i32, p, p, pool, p, p, p, p, i32, i32, i32, i32, i32, f32,
                                       p, p, sz, p]
     lib.pa_decode.argtypes = [p, i64, i32, p, p, pool, p, p, i32, i32, i32, f32, p, p, p, sz, p]
@@ -85,7 +86,7 @@ def load() -> ctypes.CDLL:
     lib.pa_status_string.restype = ctypes.c_char_p
     lib.pa_abi_version.restype = ctypes.c_int
     for fn in ("pa_store_kv", "pa_store_kv_int8", "pa_prefill_varlen", "pa_prefill_varlen_int8", "pa_decode",
-               "pa_decode_int8", "pa_decode_order", "pa_gather_kv",
+               "pa_decode_int8", "pa_decode_order", "pa_copy_blocks", "pa_gather_kv",
                "pa_validate_prefill_metadata", "pa_validate_decode_metadata"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
@@ -239,6 +240,22 @@ def pa_store_kv_int8(k, v, slot_mapping, k_pool, v_pool, k_scale, v_scale):
         _ptr(k), _row_stride(k, row, "k"), _ptr(v), _row_stride(v, row, "v"), _dtype_code(k),
         _ptr(slot_mapping), n, _ptr(k_pool), _ptr(v_pool), _ptr(k_scale), _ptr(v_scale),
         ctypes.byref(pool), _stream()))
+
+
+def pa_copy_blocks(src_blocks, dst_blocks, num_valid, k_pool, v_pool, k_scale=None, v_scale=None):
+    """Copy slots 0..num_valid[i]-1 of block src_blocks[i] to block dst_blocks[i]
+    (int32 device tensors) in the K/V pools (and the INT8 scale pools)."""
+    lib = load()
+    _dev(k_pool, v_pool)
+    pool = pool_desc_int8(k_pool, k_scale) if k_pool.dtype == torch.int8 else pool_desc(k_pool)
+    if v_pool.shape != k_pool.shape or v_pool.dtype != k_pool.dtype or not v_pool.is_contiguous():
+        raise ValueError("v_pool must match k_pool")
+    src, dst, nv = _i32(src_blocks, "src_blocks"), _i32(dst_blocks, "dst_blocks"), _i32(num_valid, "num_valid")
+    n = src.numel()
+    if dst.numel() != n or nv.numel() != n:
+        raise ValueError("src_blocks, dst_blocks and num_valid must have one entry per pair")
+    _check("pa_copy_blocks", lib.pa_copy_blocks(_ptr(k_pool), _ptr(v_pool), _ptr(k_scale), _ptr(v_scale),
+                                                ctypes.byref(pool), _ptr(src), _ptr(dst), _ptr(nv), n, _stream()))
 
 
 def pa_decode(q, k_pool, v_pool, context_lens, block_table, max_context_len, softmax_scale,

@@ -128,6 +128,34 @@ pa_status pa_store_kv_int8(const void *k, int64_t k_row_stride, const void *v, i
                                              k_pool, v_pool, k_scale, v_scale, g, (hipStream_t)stream));
 }
 
+pa_status pa_copy_blocks(void *k_pool, void *v_pool, void *k_scale, void *v_scale, const pa_pool *pool,
+                         const int32_t *src_blocks, const int32_t *dst_blocks, const int32_t *num_valid,
+                         int32_t num_pairs, void *stream) {
+    pa::PoolGeom g;
+    if (!pool) return PA_ERR_NULL_ARG;
+    const bool i8 = pool->dtype == PA_INT8;
+    pa_status st = i8 ? check_pool_int8(pool, &g) : check_pool(pool, &g);
+    if (st != PA_OK) return st;
+    if (num_pairs < 0) return PA_ERR_BAD_SHAPE;
+    if (num_pairs == 0) return PA_OK;
+    if (!k_pool || !v_pool || !src_blocks || !dst_blocks || !num_valid) return PA_ERR_NULL_ARG;
+    if (i8 && (!k_scale || !v_scale)) return PA_ERR_NULL_ARG;
+    const int64_t slot = (int64_t)g.hkv * g.d * (i8 ? 1 : elem_bytes(g.dtype));
+    hipError_t e = pa::launch_copy_blocks(k_pool, slot, g, src_blocks, dst_blocks, num_valid, num_pairs,
+                                          (hipStream_t)stream);
+    if (e == hipSuccess)
+        e = pa::launch_copy_blocks(v_pool, slot, g, src_blocks, dst_blocks, num_valid, num_pairs, (hipStream_t)stream);
+    if (e == hipSuccess && i8) {
+        const int64_t sslot = (int64_t)g.hkv * 2;
+        e = pa::launch_copy_blocks(k_scale, sslot, g, src_blocks, dst_blocks, num_valid, num_pairs,
+                                   (hipStream_t)stream);
+        if (e == hipSuccess)
+            e = pa::launch_copy_blocks(v_scale, sslot, g, src_blocks, dst_blocks, num_valid, num_pairs,
+                                       (hipStream_t)stream);
+    }
+    return from_hip(e);
+}
+
 size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t total_q, int32_t num_q_heads,
                                   int32_t max_seqlen_q, int32_t max_seqlen_k, const pa_pool *pool) {
     (void)max_seqlen_q;

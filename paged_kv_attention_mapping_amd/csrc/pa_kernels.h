@@ -31,6 +31,12 @@ hipError_t launch_store_kv_int8(const void *k, int64_t k_row_stride, const void 
                                 void *v_pool, void *k_scale, void *v_scale, const PoolGeom &g,
                                 hipStream_t stream);
 
+// Copy slots 0 .. num_valid[i]-1 of block src_blocks[i] to block
+// dst_blocks[i] in one pool whose slots are slot_bytes bytes.
+hipError_t launch_copy_blocks(void *pool, int64_t slot_bytes, const PoolGeom &g, const int32_t *src_blocks,
+                              const int32_t *dst_blocks, const int32_t *num_valid, int num_pairs,
+                              hipStream_t stream);
+
 hipError_t launch_gather_kv(const void *k_pool, const void *v_pool, const PoolGeom &g,
                             const int32_t *cu_seqlens_k, const int32_t *block_table, int bt_stride,
                             int num_seqs, int total_k, void *k_out, void *v_out, hipStream_t stream);

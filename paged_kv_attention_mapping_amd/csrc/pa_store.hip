@@ -149,7 +149,70 @@ __global__ __launch_bounds__(kStoreThreads) void store_kv_int8(
     quantize(v + t * v_stride, v_pool, v_scale);
 }
 
+// Copy-on-write of shared, mutable last blocks (vLLM/SGLang interview labs,
+// section 4, the follow-up on a native block-table fork: the child gets a new
+// block holding a copy of the valid KV; full immutable blocks are never
+// copied).  For pair i, slots 0 .. n-1 (n = num_valid[i]) of block src[i] go
+// to block dst[i].  In the [num_blocks][block_size][...] layout they are one
+// contiguous run of n * slot_bytes bytes, so a pair is a contiguous copy:
+// workgroup (pair, part) moves the 16-byte chunks part*kCopyPer*256 + i*256 +
+// thread (coalesced); a tail shorter than 16 bytes (scale pools) moves in
+// 2-byte pieces.  VEC = false (blocks not 16-byte aligned): 2-byte pieces only.
+// Pairs with ids outside the pool or n outside [1, block_size] are skipped.
+constexpr int kCopyPer = 4;  // 16-byte chunks per thread per workgroup
+template <bool VEC>
+__global__ __launch_bounds__(kStoreThreads) void copy_blocks_kernel(
+    char *__restrict__ pool, int64_t block_bytes, int64_t slot_bytes, int64_t num_blocks, int block_size,
+    const int32_t *__restrict__ src, const int32_t *__restrict__ dst, const int32_t *__restrict__ num_valid,
+    int parts) {
+    const int pair = blockIdx.x / parts, part = blockIdx.x % parts;
+    const int64_t sb = src[pair], db = dst[pair];
+    const int n = num_valid[pair];
+    if (sb < 0 || sb >= num_blocks || db < 0 || db >= num_blocks || n <= 0 || n > block_size) return;
+    const int64_t bytes = (int64_t)n * slot_bytes;
+    const char *from = pool + sb * block_bytes;
+    char *to = pool + db * block_bytes;
+    if constexpr (VEC) {
+#pragma unroll
+        for (int i = 0; i < kCopyPer; ++i) {
+            const int64_t off = ((int64_t)(part * kCopyPer + i) * kStoreThreads + threadIdx.x) * 16;
+            if (off + 16 <= bytes) {
+                *reinterpret_cast<uint4 *>(to + off) = ld16(from + off);
+            } else if (off < bytes) {
+                for (int64_t b = off; b < bytes; b += 2)
+                    *reinterpret_cast<uint16_t *>(to + b) = *reinterpret_cast<const uint16_t *>(from + b);
+            }
+        }
+    } else {
+        for (int64_t b = ((int64_t)part * kStoreThreads + threadIdx.x) * 2; b < bytes;
+             b += (int64_t)parts * kStoreThreads * 2)
+            *reinterpret_cast<uint16_t *>(to + b) = *reinterpret_cast<const uint16_t *>(from + b);
+    }
+}
+
 }  // namespace
+
+hipError_t launch_copy_blocks(void *pool, int64_t slot_bytes, const PoolGeom &g, const int32_t *src_blocks,
+                              const int32_t *dst_blocks, const int32_t *num_valid, int num_pairs,
+                              hipStream_t stream) {
+    if (num_pairs == 0 || !pool) return hipSuccess;
+    const int64_t block_bytes = slot_bytes * g.block_size;
+    const bool vec = block_bytes % 16 == 0 && aligned16(pool);
+    if (vec) {
+        const int64_t chunks = (block_bytes + 15) / 16;
+        const int parts = (int)((chunks + kStoreThreads * kCopyPer - 1) / (kStoreThreads * kCopyPer));
+        hipLaunchKernelGGL(copy_blocks_kernel<true>, dim3((unsigned)((int64_t)num_pairs * parts)), dim3(kStoreThreads),
+                           0, stream, (char *)pool, block_bytes, slot_bytes, g.num_blocks, g.block_size, src_blocks,
+                           dst_blocks, num_valid, parts);
+    } else {
+        const int64_t pieces = (block_bytes + 1) / 2;
+        const int parts = (int)((pieces + kStoreThreads * kCopyPer - 1) / (kStoreThreads * kCopyPer));
+        hipLaunchKernelGGL(copy_blocks_kernel<false>, dim3((unsigned)((int64_t)num_pairs * parts)), dim3(kStoreThreads),
+                           0, stream, (char *)pool, block_bytes, slot_bytes, g.num_blocks, g.block_size, src_blocks,
+                           dst_blocks, num_valid, parts);
+    }
+    return hipGetLastError();
+}
 
 hipError_t launch_store_kv_int8(const void *k, int64_t k_row_stride, const void *v, int64_t v_row_stride,
                                 int src_dtype, const int32_t *slot_mapping, int num_tokens, void *k_pool,

@@ -101,6 +101,20 @@ def test_int8_prefill_host_errors():
                                  8, 2, 10, 5, 5, 0.1, dummy, None, 0, None) == 3
 
 
+def test_copy_blocks_host_errors():
+    lib = pa.load()
+    dummy = ctypes.c_void_p(4096)
+    bf = _pool(dtype=pa.PA_BF16)
+    i8 = _pool(dtype=pa.PA_INT8)
+    assert lib.pa_copy_blocks(dummy, dummy, None, None, None, dummy, dummy, dummy, 1, None) == 1
+    assert lib.pa_copy_blocks(dummy, dummy, None, None, ctypes.byref(_pool(dtype=9)), dummy, dummy, dummy, 1,
+                              None) == 3
+    assert lib.pa_copy_blocks(dummy, dummy, None, None, ctypes.byref(bf), dummy, dummy, dummy, -1, None) == 2
+    assert lib.pa_copy_blocks(None, None, None, None, ctypes.byref(bf), None, None, None, 0, None) == 0
+    assert lib.pa_copy_blocks(dummy, dummy, None, None, ctypes.byref(i8), dummy, dummy, dummy, 1, None) == 1
+    assert lib.pa_copy_blocks(dummy, None, None, None, ctypes.byref(bf), dummy, dummy, dummy, 1, None) == 1
+
+
 def test_host_argument_errors_return_before_launch():
     lib = pa.load()
     pool = _pool()
