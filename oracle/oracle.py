@@ -1,7 +1,7 @@
 """ctypes wrapper over pa_oracle.c (fp64 CPU reference).
 
 TEST INFRASTRUCTURE ONLY.  Arrays are numpy; bf16 data travels as uint16 bit
-patterns, fp32 as float32.  Every function checks the C return code and
+patterns, fp16 as float16, fp32 as float32.  Every function checks the C return code and
 raises on failure.  The C source says which page and section each step
 follows.
 """
@@ -15,6 +15,7 @@ import numpy as np
 
 F32 = 0
 BF16 = 1
+F16 = 3
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "pa_oracle.c")
@@ -70,7 +71,9 @@ def _dtype_code(a: np.ndarray) -> int:
         return F32
     if a.dtype == np.uint16:
         return BF16
-    raise TypeError(f"oracle takes float32 or uint16 (bf16 bits), got {a.dtype}")
+    if a.dtype == np.float16:
+        return F16
+    raise TypeError(f"oracle takes float32, float16 or uint16 (bf16 bits), got {a.dtype}")
 
 
 def _ptr(a):

@@ -32,7 +32,10 @@
  * tiling, no online rescaling, no reordering.
  *
  * Element types: 0 = fp32, 1 = bf16 (raw 16-bit patterns; widened exactly to
- * fp64 by placing the bits in the top half of an fp32).
+ * fp64 by placing the bits in the top half of an fp32), 3 = IEEE binary16
+ * (raw 16-bit patterns; widened exactly from sign, 5-bit exponent and 10-bit
+ * fraction).  Code 2 is unused here: the INT8 reference dequantizes in Python
+ * and hands this file fp32 pools.
  *
  * Return codes: 0 ok, 1 null argument, 2 bad shape / sizes,
  *               3 bad element type, 4 index out of range in the metadata.
@@ -50,7 +53,7 @@ enum { OR_OK = 0, OR_NULL = 1, OR_SHAPE = 2, OR_DTYPE = 3, OR_RANGE = 4 };
 static int elem_bytes_of(int dtype)
 {
     if (dtype == 0) return 4;
-    if (dtype == 1) return 2;
+    if (dtype == 1 || dtype == 3) return 2;
     return 0;
 }
 
@@ -64,6 +67,16 @@ static double widen(const void *base, int64_t index, int dtype)
     }
     uint16_t h;
     memcpy(&h, (const char *)base + index * 2, 2);
+    if (dtype == 3) {
+        /* binary16: (-1)^s * 2^(e-15) * (1 + f/1024) for 0 < e < 31,
+         * (-1)^s * 2^-14 * (f/1024) for e == 0, inf / NaN for e == 31. */
+        int sign = h >> 15, e = (h >> 10) & 31, f = h & 1023;
+        double mag;
+        if (e == 31) mag = f ? NAN : INFINITY;
+        else if (e == 0) mag = ldexp((double)f, -24);
+        else mag = ldexp((double)(1024 + f), e - 25);
+        return sign ? -mag : mag;
+    }
     uint32_t bits = (uint32_t)h << 16;
     float f;
     memcpy(&f, &bits, 4);

@@ -73,7 +73,7 @@ def test_gather_worked_example_left_pad():
 
 @settings(max_examples=40, deadline=None)
 @given(seed=st.integers(0, 2**31 - 1), bs=st.sampled_from([1, 2, 4, 16]),
-       hkv=st.integers(1, 3), d=st.sampled_from([1, 4, 8]), dtype=st.sampled_from(["f32", "bf16"]),
+       hkv=st.integers(1, 3), d=st.sampled_from([1, 4, 8]), dtype=st.sampled_from(["f32", "bf16", "f16"]),
        lens=st.lists(st.integers(1, 40), min_size=1, max_size=4))
 def test_store_gather_roundtrip_bitwise(seed, bs, hkv, d, dtype, lens):
     """Store then gather returns the exact bits; untouched slots keep their bits."""
@@ -108,7 +108,7 @@ def test_store_rejects_out_of_range_slot():
 
 # ---------------------------------------------------------------- attention
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("hq,hkv", [(4, 2), (4, 4), (8, 2), (3, 1)])
 def test_identity_table_equals_textbook_causal_sdpa(dtype, hq, hkv):
     """With q_offsets 0 the paged result is dense causal attention
@@ -307,7 +307,7 @@ def test_decode_zero_context_is_zero():
     assert (out[1] == 0).all() and np.isfinite(out).all()
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 def test_decode_equals_unmasked_sdpa_over_context(dtype):
     """A decode query sits at the last position, so it sees every key of its
     context (nano-vllm Step 5, prepare_decode: context length = len(seq)):

@@ -8,7 +8,8 @@ and draws N(0,1) values.  Everything is a pure function of the seed.
 
 Data conventions
   * bf16 tensors travel as uint16 bit patterns (numpy has no bf16); values are
-    drawn in fp32 and rounded to nearest-even to bf16.
+    drawn in fp32 and rounded to nearest-even to bf16.  fp16 tensors are numpy
+    float16 (the same fp32 draw, rounded to nearest-even by numpy's cast).
   * Pools are [num_blocks, block_size, num_kv_heads, head_dim]; every slot no
     sequence uses is filled with a quiet-NaN pattern ("poisoned").
   * block_table rows are padded past a sequence's last block with the id of a
@@ -25,6 +26,7 @@ from dataclasses import dataclass, field
 import numpy as np
 
 NAN_BF16 = np.uint16(0x7FC0)
+NAN_F16 = np.uint16(0x7E00)
 NAN_F32_BITS = np.uint32(0x7FC00000)
 
 # Qwen3-0.6B attention shapes: 28 layers, 16 query heads, 8 KV heads, head_dim 128.
@@ -50,17 +52,25 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
 
 
 def np_dtype(dtype: str):
-    return {"bf16": np.uint16, "f32": np.float32}[dtype]
+    return {"bf16": np.uint16, "f16": np.float16, "f32": np.float32}[dtype]
+
+
+def elem_bytes(dtype: str) -> int:
+    return 4 if dtype == "f32" else 2
 
 
 def normal(rng: np.random.Generator, shape, dtype: str) -> np.ndarray:
     x = rng.standard_normal(size=shape, dtype=np.float32)
-    return f32_to_bf16_bits(x) if dtype == "bf16" else x
+    if dtype == "bf16":
+        return f32_to_bf16_bits(x)
+    return x.astype(np.float16) if dtype == "f16" else x
 
 
 def poisoned_pool(num_blocks: int, block_size: int, hkv: int, d: int, dtype: str) -> np.ndarray:
     if dtype == "bf16":
         return np.full((num_blocks, block_size, hkv, d), NAN_BF16, dtype=np.uint16)
+    if dtype == "f16":
+        return np.full((num_blocks, block_size, hkv, d), NAN_F16, dtype=np.uint16).view(np.float16)
     return np.full((num_blocks, block_size, hkv, d), NAN_F32_BITS, dtype=np.uint32).view(np.float32)
 
 
@@ -189,7 +199,7 @@ class DecodeCase:
 
     def kv_bytes(self):
         """Bytes of K and V one decode pass must read: each visible row once per KV head."""
-        eb = 2 if self.dtype == "bf16" else 4
+        eb = elem_bytes(self.dtype)
         return int(self.context_lens.astype(np.int64).sum()) * self.num_kv_heads * self.head_dim * eb * 2
 
     def empty_pools(self):
@@ -363,4 +373,6 @@ def device_normal(shape, seed, device="cuda", dtype="bf16"):
     g = torch.Generator(device=device)
     g.manual_seed(int(seed))
     t = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
-    return t.to(torch.bfloat16) if dtype == "bf16" else t
+    if dtype == "bf16":
+        return t.to(torch.bfloat16)
+    return t.to(torch.float16) if dtype == "f16" else t
