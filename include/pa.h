@@ -34,12 +34,16 @@
  * block_table[s][j / block_size] at offset j % block_size (same page,
  * Step 1, "why block_table"); its flat slot is block * block_size + offset.
  *
- * Supported: dtype PA_F32 or PA_BF16; head_dim 32, 64, 128 or 256;
+ * Supported: dtype PA_F32, PA_BF16 or PA_F16 (IEEE binary16, the element
+ * type of the fork's fused-dequantization microbenchmark: LLM inference
+ * interview notes (nano-vllm fork), Q3, the INT8-versus-FP16 latency table);
+ * head_dim 32, 64, 128 or 256;
  * block_size a power of two (1 .. 65536); num_q_heads a multiple of
  * num_kv_heads with group size num_q_heads / num_kv_heads in {1, 2, 4, 8}.
  * Query head h reads KV head h / (num_q_heads / num_kv_heads).
  * The bf16 prefill runs on MFMA for head_dim 64 and 128; every other
- * supported shape runs on the vector ALU path.
+ * supported shape runs on the vector ALU path.  Outputs of a 16-bit type are
+ * the fp32 result rounded to nearest even (fp16: beyond +-65504 it is +-inf).
  */
 #ifndef PA_H
 #define PA_H
@@ -51,7 +55,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 3
+#define PA_ABI_VERSION 4
 
 typedef enum {
     PA_OK = 0,
@@ -64,7 +68,7 @@ typedef enum {
     PA_ERR_BAD_METADATA = 7  /* (validators only) host copy of metadata invalid */
 } pa_status;
 
-typedef enum { PA_F32 = 0, PA_BF16 = 1, PA_INT8 = 2 } pa_dtype;
+typedef enum { PA_F32 = 0, PA_BF16 = 1, PA_INT8 = 2, PA_F16 = 3 } pa_dtype;
 
 /* Shape of one layer's K pool (the V pool has the same shape). Host struct. */
 typedef struct {
@@ -114,13 +118,14 @@ pa_status pa_store_kv(const void *k, int64_t k_row_stride,
  * scales below fp16's range store as 0, whose codes are all 0 anyway).
  *
  *   k, v          [num_tokens][num_kv_heads][head_dim] rows of src_dtype
- *                 (PA_BF16 or PA_F32), strides in elements as in pa_store_kv;
+ *                 (PA_BF16, PA_F16 or PA_F32), strides in elements as in
+ *                 pa_store_kv;
  *                 values must be finite and |x| <= 65504 * 127.
  *   slot_mapping  int32 [num_tokens]; -1 = padding token, skipped.
  *   k_pool,v_pool int8 code pools, 8-byte aligned; k_scale,v_scale fp16
  *                 scale pools; all written in place.
  *   pool          dtype PA_INT8; head_dim a multiple of 8, at most 256.
- * Errors: PA_ERR_BAD_DTYPE (pool not PA_INT8, src_dtype not bf16/fp32),
+ * Errors: PA_ERR_BAD_DTYPE (pool not PA_INT8, src_dtype not bf16/fp16/fp32),
  * PA_ERR_UNSUPPORTED (head_dim, block_size, misaligned pools), the checks of
  * pa_store_kv otherwise.  Slots must be unique within one call.
  */
@@ -138,8 +143,9 @@ pa_status pa_store_kv_int8(const void *k, int64_t k_row_stride,
  * code * float(scale).  As the pages suggest, the K scale multiplies each
  * finished dot product and the V scale is folded into the probability.
  *
- *   q, out        [num_seqs][num_q_heads][head_dim] of q_dtype (PA_BF16 or
- *                 PA_F32); q rows at q_row_stride elements, 16-byte aligned;
+ *   q, out        [num_seqs][num_q_heads][head_dim] of q_dtype (PA_BF16,
+ *                 PA_F16 or PA_F32); q rows at q_row_stride elements, 16-byte
+ *                 aligned;
  *                 bf16 q values must lie within fp16's range (|q| <= 65504;
  *                 the K dot products run on fp16 pairs).
  *   k_pool,v_pool int8 code pools, 16-byte aligned; k_scale,v_scale fp16
@@ -164,10 +170,13 @@ pa_status pa_decode_int8(const void *q, int64_t q_row_stride, int32_t num_q_head
  * dequantization fused into the attention instead of first gathering the
  * referenced K/V into a float tensor (the slow path the same answer, part 3,
  * describes for prefill).  Same arguments, semantics and errors as
- * pa_prefill_varlen, plus q_dtype (PA_BF16 / PA_F32, also out's type) and the
- * fp16 scale pools; INT8 pools as for pa_decode_int8 (query groups 1, 2, 4).
- * Each packed query token is one row of the INT8 decode pass over its
- * visible keys (vector ALU, not the matrix cores).
+ * pa_prefill_varlen, plus q_dtype (PA_BF16 / PA_F16 / PA_F32, also out's
+ * type) and the fp16 scale pools; INT8 pools as for pa_decode_int8 (query
+ * groups 1, 2, 4).  bf16 queries with head_dim 64 or 128, an even number of
+ * KV heads, a 16-byte aligned out and 4-byte aligned scale pools run on the
+ * matrix cores (each key step's codes are dequantized to bf16 in LDS); every
+ * other call takes each packed query token as one row of the INT8 decode pass
+ * over its visible keys (vector ALU).
  */
 size_t pa_prefill_int8_workspace_bytes(int32_t num_seqs, int32_t total_q, int32_t num_q_heads,
                                        int32_t max_seqlen_k, const pa_pool *pool /* host */);

@@ -37,16 +37,18 @@ _FLOOR = np.float32(1.0e-8)
 
 
 def widen(x: np.ndarray) -> np.ndarray:
-    """Exact fp32 view of stored model values (bf16 bit patterns or fp32)."""
+    """Exact fp32 view of stored model values (bf16 bit patterns, fp16 or fp32)."""
     x = np.asarray(x)
     if x.dtype == np.uint16:
         return (x.astype(np.uint32) << 16).view(np.float32)
+    if x.dtype == np.float16:
+        return x.astype(np.float32)
     assert x.dtype == np.float32
     return x
 
 
 def quantize(x: np.ndarray):
-    """Quantize head vectors x[..., head_dim] (bf16 bits or fp32).
+    """Quantize head vectors x[..., head_dim] (bf16 bits, fp16 or fp32).
 
     Returns (codes int8 [..., head_dim], scale float32 [...], stored scale
     float16 [...]).
@@ -98,12 +100,12 @@ def dequantize_pools(kq_pool, vq_pool, ks_pool, vs_pool):
 
 def prefill(q, kq_pool, vq_pool, ks_pool, vs_pool, cu_seqlens_q, cu_seqlens_k, q_offsets, block_table, scale,
             rows=None):
-    """fp64 causal attention of q (bf16 bits or fp32) over the dequantized pools."""
+    """fp64 causal attention of q (bf16 bits, fp16 or fp32) over the dequantized pools."""
     kf, vf = dequantize_pools(kq_pool, vq_pool, ks_pool, vs_pool)
     return _o.prefill(widen(q), kf, vf, cu_seqlens_q, cu_seqlens_k, q_offsets, block_table, scale, rows=rows)
 
 
 def decode(q, kq_pool, vq_pool, ks_pool, vs_pool, context_lens, block_table, scale, seqs=None):
-    """fp64 decode attention of q (bf16 bits or fp32) over the dequantized pools."""
+    """fp64 decode attention of q (bf16 bits, fp16 or fp32) over the dequantized pools."""
     kf, vf = dequantize_pools(kq_pool, vq_pool, ks_pool, vs_pool)
     return _o.decode(widen(q), kf, vf, context_lens, block_table, scale, seqs=seqs)

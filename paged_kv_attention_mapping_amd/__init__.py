@@ -9,6 +9,7 @@ from ._lib import (  # noqa: F401
     EXPORTS,
     LIB_PATH,
     PA_BF16,
+    PA_F16,
     PA_F32,
     PA_INT8,
     PaError,

@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(_PKG, "libpa.so")
 PA_F32 = 0
 PA_BF16 = 1
 PA_INT8 = 2
+PA_F16 = 3
 
 _STATUS = {
     0: "PA_OK", 1: "PA_ERR_NULL_ARG", 2: "PA_ERR_BAD_SHAPE", 3: "PA_ERR_BAD_DTYPE",
@@ -100,7 +101,9 @@ def _dtype_code(t: torch.Tensor) -> int:
         return PA_F32
     if t.dtype == torch.bfloat16:
         return PA_BF16
-    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+    if t.dtype == torch.float16:
+        return PA_F16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32, bfloat16 or float16)")
 
 
 def pool_desc(k_pool: torch.Tensor) -> PaPool:
@@ -220,7 +223,7 @@ def pa_prefill_varlen(q, k_pool, v_pool, cu_seqlens_q, cu_seqlens_k, q_offsets, 
 
 
 def pa_store_kv_int8(k, v, slot_mapping, k_pool, v_pool, k_scale, v_scale):
-    """Quantize k/v [T, Hkv, D] (bf16 or fp32) per (token, KV head) into the
+    """Quantize k/v [T, Hkv, D] (bf16, fp16 or fp32) per (token, KV head) into the
     INT8 code pools and fp16 scale pools at slot_mapping (int32, -1 = skip)."""
     lib = load()
     _dev(k, v, k_pool, v_pool, k_scale, v_scale)
@@ -294,7 +297,7 @@ def pa_decode_int8_workspace_bytes(num_seqs, num_q_heads, max_context_len, k_poo
 
 def pa_decode_int8(q, k_pool, v_pool, k_scale, v_scale, context_lens, block_table, max_context_len,
                    softmax_scale, out=None, workspace=None, row_order=None):
-    """pa_decode over INT8 pools (int8 codes, fp16 scales); q/out bf16 or fp32."""
+    """pa_decode over INT8 pools (int8 codes, fp16 scales); q/out bf16, fp16 or fp32."""
     lib = load()
     _dev(q, k_pool, v_pool, k_scale, v_scale)
     pool = pool_desc_int8(k_pool, k_scale)
@@ -326,7 +329,7 @@ def pa_decode_int8(q, k_pool, v_pool, k_scale, v_scale, context_lens, block_tabl
 
 def pa_prefill_varlen_int8(q, k_pool, v_pool, k_scale, v_scale, cu_seqlens_q, cu_seqlens_k, q_offsets,
                            block_table, max_seqlen_q, max_seqlen_k, softmax_scale, out=None, workspace=None):
-    """pa_prefill_varlen over INT8 pools (int8 codes, fp16 scales); q/out bf16 or fp32."""
+    """pa_prefill_varlen over INT8 pools (int8 codes, fp16 scales); q/out bf16, fp16 or fp32."""
     lib = load()
     _dev(q, k_pool, v_pool, k_scale, v_scale)
     pool = pool_desc_int8(k_pool, k_scale)

@@ -24,7 +24,10 @@ int log2i(int64_t x) {
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
-int elem_bytes(int dtype) { return dtype == PA_F32 ? 4 : (dtype == PA_BF16 ? 2 : 0); }
+int elem_bytes(int dtype) { return dtype == PA_F32 ? 4 : (dtype == PA_BF16 || dtype == PA_F16 ? 2 : 0); }
+
+// Element types of the queries and of the rows quantized into INT8 pools.
+bool float_dtype(int dtype) { return dtype == PA_F32 || dtype == PA_BF16 || dtype == PA_F16; }
 
 // Checks shared by every call that reads the pools.
 pa_status check_pool(const pa_pool *pool, pa::PoolGeom *g) {
@@ -115,7 +118,7 @@ pa_status pa_store_kv_int8(const void *k, int64_t k_row_stride, const void *v, i
     pa::PoolGeom g;
     pa_status st = check_pool_int8(pool, &g);
     if (st != PA_OK) return st;
-    if (src_dtype != PA_F32 && src_dtype != PA_BF16) return PA_ERR_BAD_DTYPE;
+    if (!float_dtype(src_dtype)) return PA_ERR_BAD_DTYPE;
     if (num_tokens < 0) return PA_ERR_BAD_SHAPE;
     if (g.d % 8 || g.d > 256) return PA_ERR_UNSUPPORTED;
     if (num_tokens == 0) return PA_OK;
@@ -246,7 +249,7 @@ pa_status pa_decode(const void *q, int64_t q_row_stride, int32_t num_q_heads, co
 pa_status check_decode_int8_shape(const pa_pool *pool, int32_t num_q_heads, int32_t q_dtype, pa::PoolGeom *g) {
     pa_status st = check_pool_int8(pool, g);
     if (st != PA_OK) return st;
-    if (q_dtype != PA_F32 && q_dtype != PA_BF16) return PA_ERR_BAD_DTYPE;
+    if (!float_dtype(q_dtype)) return PA_ERR_BAD_DTYPE;
     if (num_q_heads <= 0 || num_q_heads % g->hkv) return PA_ERR_BAD_SHAPE;
     const int group = num_q_heads / g->hkv;
     if (group != 1 && group != 2 && group != 4) return PA_ERR_UNSUPPORTED;

@@ -134,8 +134,8 @@ struct RowArgs {
 };
 
 // This lane's slice of one query head, kept in the form the dot product wants:
-// bf16 stays packed (two elements per 32-bit word, consumed by v_dot2_f32_bf16);
-// fp32 is kept as floats.
+// bf16 and fp16 stay packed (two elements per 32-bit word, consumed by
+// v_dot2_f32_bf16 / v_dot2_f32_f16); fp32 is kept as floats.
 template <typename T> struct QSlice;
 template <> struct QSlice<bf16_t> {
     uint4 w;
@@ -147,6 +147,19 @@ template <> struct QSlice<bf16_t> {
         acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w.y), __builtin_bit_cast(bf16x2, k.y), acc, false);
         acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w.z), __builtin_bit_cast(bf16x2, k.z), acc, false);
         acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w.w), __builtin_bit_cast(bf16x2, k.w), acc, false);
+        return acc;
+    }
+};
+template <> struct QSlice<f16_t> {   // fp16: v_dot2_f32_f16 on the packed pairs
+    uint4 w;
+    __device__ __forceinline__ void load(const f16_t *p) { w = ld16(p); }
+    __device__ __forceinline__ float dot(const uint4 &k) const {
+        typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+        float acc = 0.f;
+        acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w.x), __builtin_bit_cast(f16x2, k.x), acc, false);
+        acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w.y), __builtin_bit_cast(f16x2, k.y), acc, false);
+        acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w.z), __builtin_bit_cast(f16x2, k.z), acc, false);
+        acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w.w), __builtin_bit_cast(f16x2, k.w), acc, false);
         return acc;
     }
 };
@@ -415,8 +428,9 @@ __global__ __launch_bounds__(NW * kWave) void row_attn_int8(RowArgs a, Rows rows
         }
     }
     // this lane's 16 elements of each query head, as fp32, and their sum
-    // (bf16 queries: as fp16 pairs for v_dot2_f32_f16, summed as fp16 values)
-    constexpr bool kF16Dot = std::is_same<TQ, bf16_t>::value;
+    // (bf16 and fp16 queries: as fp16 pairs for v_dot2_f32_f16, summed as fp16
+    // values; exact for fp16 queries)
+    constexpr bool kF16Dot = std::is_same<TQ, bf16_t>::value || std::is_same<TQ, f16_t>::value;
     typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
     float qv[G][EPV], qsum[G];
     half2_t qh[G][EPV / 2];
@@ -685,7 +699,7 @@ __global__ __launch_bounds__(kThreads) void row_attn_merge(MergeArgs a, Rows row
 }
 
 int tokens_per_round(int dtype, int d, int nw) {
-    const int epv = dtype == 0 ? 4 : (dtype == 1 ? 8 : 16);  // fp32, bf16, int8
+    const int epv = dtype == 0 ? 4 : (dtype == 2 ? 16 : 8);  // fp32, int8, else 16-bit
     const int lpt = d / epv;
     return nw * (kWave / lpt) * kUnroll;
 }
@@ -747,8 +761,9 @@ hipError_t dispatch_dim(int d, int group, int waves, const RowArgs &a, const Row
 template <class Rows>
 hipError_t dispatch(const PoolGeom &g, int group, int waves, const RowArgs &a, const Rows &rows,
                     hipStream_t s) {
-    return g.dtype == 0 ? dispatch_dim<float>(g.d, group, waves, a, rows, s)
-                        : dispatch_dim<bf16_t>(g.d, group, waves, a, rows, s);
+    if (g.dtype == 0) return dispatch_dim<float>(g.d, group, waves, a, rows, s);
+    if (g.dtype == 3) return dispatch_dim<f16_t>(g.d, group, waves, a, rows, s);
+    return dispatch_dim<bf16_t>(g.d, group, waves, a, rows, s);
 }
 
 RowArgs make_args(const void *q, int64_t q_row_stride, int hq, const void *k_pool, const void *v_pool,
@@ -844,8 +859,9 @@ hipError_t launch_decode_int8(const void *q, int64_t q_row_stride, int hq, int q
     a.v_scale = reinterpret_cast<const _Float16 *>(v_scale);
     const DecodeRows rows{context_lens, row_order};
     const int group = hq / g.hkv;
-    return q_dtype == 0 ? dispatch_dim<float, DecodeRows, true>(g.d, group, plan.waves, a, rows, stream)
-                        : dispatch_dim<bf16_t, DecodeRows, true>(g.d, group, plan.waves, a, rows, stream);
+    if (q_dtype == 0) return dispatch_dim<float, DecodeRows, true>(g.d, group, plan.waves, a, rows, stream);
+    if (q_dtype == 3) return dispatch_dim<f16_t, DecodeRows, true>(g.d, group, plan.waves, a, rows, stream);
+    return dispatch_dim<bf16_t, DecodeRows, true>(g.d, group, plan.waves, a, rows, stream);
 }
 
 hipError_t launch_decode_order(const int32_t *context_lens, int num_rows, int32_t *row_order,
@@ -881,8 +897,9 @@ hipError_t launch_prefill_rows_int8(const void *q, int64_t q_row_stride, int hq,
     a.v_scale = reinterpret_cast<const _Float16 *>(v_scale);
     const PrefillRows rows{cu_seqlens_q, cu_seqlens_k, q_offsets, num_seqs};
     const int group = hq / g.hkv;
-    return q_dtype == 0 ? dispatch_dim<float, PrefillRows, true>(g.d, group, plan.waves, a, rows, stream)
-                        : dispatch_dim<bf16_t, PrefillRows, true>(g.d, group, plan.waves, a, rows, stream);
+    if (q_dtype == 0) return dispatch_dim<float, PrefillRows, true>(g.d, group, plan.waves, a, rows, stream);
+    if (q_dtype == 3) return dispatch_dim<f16_t, PrefillRows, true>(g.d, group, plan.waves, a, rows, stream);
+    return dispatch_dim<bf16_t, PrefillRows, true>(g.d, group, plan.waves, a, rows, stream);
 }
 
 }  // namespace pa

@@ -11,15 +11,23 @@ constexpr int kWave = 64;
 
 // Storage tags: the kernels move raw bits and widen to fp32 themselves.
 struct bf16_t { uint16_t bits; };
+struct f16_t { uint16_t bits; };   // IEEE binary16
 
 template <typename T> struct Elem;
 template <> struct Elem<float> { static constexpr int bytes = 4; };
 template <> struct Elem<bf16_t> { static constexpr int bytes = 2; };
+template <> struct Elem<f16_t> { static constexpr int bytes = 2; };
 
 // ---- conversions ----------------------------------------------------------
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// binary16 halves of a 32-bit word, widened exactly (v_cvt_f32_f16).
+__device__ __forceinline__ float f16_lo(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)w); }
+__device__ __forceinline__ float f16_hi(uint32_t w) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+}
 
 // fp32 -> bf16 bits, round to nearest, ties to even; NaN stays a quiet NaN.
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
@@ -32,6 +40,7 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
 // One stored element as fp32 (exact).
 __device__ __forceinline__ float to_float(float x) { return x; }
 __device__ __forceinline__ float to_float(bf16_t x) { return bf16_lo(x.bits); }
+__device__ __forceinline__ float to_float(f16_t x) { return f16_lo(x.bits); }
 
 // Unpack one 16-byte vector into its elements as fp32.
 template <typename T> __device__ __forceinline__ void unpack16(const uint4 &v, float *f);
@@ -43,11 +52,20 @@ template <> __device__ __forceinline__ void unpack16<bf16_t>(const uint4 &v, flo
     f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x); f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
     f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z); f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
 }
+template <> __device__ __forceinline__ void unpack16<f16_t>(const uint4 &v, float *f) {
+    f[0] = f16_lo(v.x); f[1] = f16_hi(v.x); f[2] = f16_lo(v.y); f[3] = f16_hi(v.y);
+    f[4] = f16_lo(v.z); f[5] = f16_hi(v.z); f[6] = f16_lo(v.w); f[7] = f16_hi(v.w);
+}
 
 template <typename T> __device__ __forceinline__ void store_elem(T *p, float x);
 template <> __device__ __forceinline__ void store_elem<float>(float *p, float x) { *p = x; }
 template <> __device__ __forceinline__ void store_elem<bf16_t>(bf16_t *p, float x) {
     p->bits = (uint16_t)f32_to_bf16_bits(x);
+}
+// fp32 -> binary16, round to nearest even (v_cvt_f16_f32 in the default mode);
+// beyond the largest finite value the result is infinite.
+template <> __device__ __forceinline__ void store_elem<f16_t>(f16_t *p, float x) {
+    p->bits = __builtin_bit_cast(uint16_t, (_Float16)x);
 }
 
 // ---- cross-lane reductions (DPP inside a row of 16 lanes) -----------------

@@ -16,7 +16,7 @@ struct PoolGeom {
     int block_shift;   // log2(block_size)
     int hkv;
     int d;
-    int dtype;         // 0 fp32, 1 bf16, 2 int8 (with fp16 scale pools)
+    int dtype;         // 0 fp32, 1 bf16, 2 int8 (with fp16 scale pools), 3 fp16
 };
 
 // Store / gather ---------------------------------------------------------
@@ -24,7 +24,7 @@ hipError_t launch_store_kv(const void *k, int64_t k_row_stride, const void *v, i
                            const int32_t *slot_mapping, int num_tokens, void *k_pool, void *v_pool,
                            const PoolGeom &g, hipStream_t stream);
 
-// INT8 pools: quantize K/V rows (src_dtype 0 fp32, 1 bf16) per (token, KV
+// INT8 pools: quantize K/V rows (src_dtype 0 fp32, 1 bf16, 3 fp16) per (token, KV
 // head) into int8 codes and fp16 scales.
 hipError_t launch_store_kv_int8(const void *k, int64_t k_row_stride, const void *v, int64_t v_row_stride,
                                 int src_dtype, const int32_t *slot_mapping, int num_tokens, void *k_pool,
@@ -62,7 +62,7 @@ hipError_t launch_decode(const void *q, int64_t q_row_stride, int hq, const void
                          hipStream_t stream);
 
 // Decode over INT8 pools (int8 codes, fp16 scales per (token, KV head));
-// q and out are q_dtype (0 fp32, 1 bf16); query groups of 1, 2 or 4.
+// q and out are q_dtype (0 fp32, 1 bf16, 3 fp16); query groups of 1, 2 or 4.
 hipError_t launch_decode_int8(const void *q, int64_t q_row_stride, int hq, int q_dtype, const void *k_pool,
                               const void *v_pool, const void *k_scale, const void *v_scale, const PoolGeom &g,
                               const int32_t *context_lens, const int32_t *block_table, int bt_stride,

@@ -238,6 +238,8 @@ hipError_t launch_store_kv_int8(const void *k, int64_t k_row_stride, const void 
     };
     if (src_dtype == 0) {
         if (vec) go(float{}, std::true_type{}); else go(float{}, std::false_type{});
+    } else if (src_dtype == 3) {
+        if (vec) go(f16_t{}, std::true_type{}); else go(f16_t{}, std::false_type{});
     } else {
         if (vec) go(bf16_t{}, std::true_type{}); else go(bf16_t{}, std::false_type{});
     }
@@ -248,7 +250,7 @@ hipError_t launch_store_kv(const void *k, int64_t k_row_stride, const void *v, i
                            const int32_t *slot_mapping, int num_tokens, void *k_pool, void *v_pool,
                            const PoolGeom &g, hipStream_t stream) {
     if (num_tokens == 0) return hipSuccess;
-    const int eb = g.dtype == 0 ? 4 : 2;
+    const int eb = g.dtype == 0 ? 4 : 2;  // fp32, else bf16 / fp16
     const int row_elems = g.hkv * g.d;
     const int64_t row_bytes = (int64_t)row_elems * eb;
     const int64_t num_slots = g.num_blocks << g.block_shift;
@@ -283,7 +285,7 @@ hipError_t launch_gather_kv(const void *k_pool, const void *v_pool, const PoolGe
                             const int32_t *cu_seqlens_k, const int32_t *block_table, int bt_stride,
                             int num_seqs, int total_k, void *k_out, void *v_out, hipStream_t stream) {
     if (total_k == 0 || num_seqs == 0) return hipSuccess;
-    const int eb = g.dtype == 0 ? 4 : 2;
+    const int eb = g.dtype == 0 ? 4 : 2;  // fp32, else bf16 / fp16
     const int cpr = g.hkv * g.d * eb / 16;  // supported head_dim keeps rows a multiple of 16 B
     const int64_t n = (int64_t)total_k * cpr;
     const unsigned grid = (unsigned)((n + kStoreThreads - 1) / kStoreThreads);

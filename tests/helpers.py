@@ -8,6 +8,10 @@ import workloads as W
 
 BF16_TOL = 2e-2   # max-abs, bf16 attention outputs
 F32_TOL = 1e-5    # max-abs, fp32 attention outputs
+# max-abs, fp16 attention outputs: half an fp16 ulp of outputs below 8 in
+# magnitude (2^-9) plus the fp16 rounding of the probabilities on the matrix
+# cores (relative 2^-12 each, in numerator and denominator, on |v| < 5).
+F16_TOL = 5e-3
 
 
 def to_dev(a: np.ndarray, device="cuda") -> torch.Tensor:
@@ -32,7 +36,7 @@ def as_f64(a) -> np.ndarray:
 
 
 def tol(dtype: str) -> float:
-    return BF16_TOL if dtype == "bf16" else F32_TOL
+    return {"bf16": BF16_TOL, "f16": F16_TOL}.get(dtype, F32_TOL)
 
 
 def max_abs_err(gpu_out, ref: np.ndarray) -> float:

@@ -28,7 +28,7 @@ def test_library_loads_and_exports_every_symbol():
     lib = pa.load()
     for name in _declared_symbols():
         assert hasattr(lib, name), name
-    assert lib.pa_abi_version() == 3
+    assert lib.pa_abi_version() == 4
     assert lib.pa_status_string(0) == b"ok"
     assert b"workspace" in lib.pa_status_string(5)
 
@@ -47,7 +47,7 @@ def test_int8_store_host_errors():
     a = list(args); a[11] = ctypes.byref(_pool(d=128, dtype=pa.PA_BF16))
     assert lib.pa_store_kv_int8(*a) == 3                       # pool not INT8
     a = list(args); a[4] = pa.PA_INT8
-    assert lib.pa_store_kv_int8(*a) == 3                       # source must be bf16 / fp32
+    assert lib.pa_store_kv_int8(*a) == 3                       # source must be bf16 / fp16 / fp32
     a = list(args); a[11] = ctypes.byref(_pool(d=36, dtype=pa.PA_INT8))
     assert lib.pa_store_kv_int8(*a) == 4                       # head_dim % 8
     a = list(args); a[6] = 0
@@ -99,6 +99,27 @@ def test_int8_prefill_host_errors():
     assert call(i8, n=0) == 0 and call(i8, tq=0) == 0
     assert lib.pa_prefill_varlen(dummy, 16 * 128, 16, dummy, dummy, ctypes.byref(i8), dummy, dummy, dummy, dummy,
                                  8, 2, 10, 5, 5, 0.1, dummy, None, 0, None) == 3
+
+
+def test_f16_pools_and_queries_pass_the_dtype_checks():
+    """PA_F16 pools and fp16 INT8 sources / queries get past the element-type
+    check and stop at the next one (a null pointer), before any launch."""
+    lib = pa.load()
+    f16 = _pool(nb=8, bs=16, hkv=2, d=64, dtype=pa.PA_F16)
+    assert lib.pa_store_kv(None, 128, None, 128, None, 1, None, None, ctypes.byref(f16), None) == 1
+    assert lib.pa_gather_kv(None, None, ctypes.byref(f16), None, None, 1, 1, 1, None, None, None) == 1
+    assert lib.pa_decode(None, 128, 2, None, None, ctypes.byref(f16), None, None, 1, 1, 1, 0.1, None, None,
+                         None, 0, None) == 1
+    assert lib.pa_decode_workspace_bytes(64, 16, 32768, ctypes.byref(_pool(nb=1, hkv=8, d=128,
+                                                                           dtype=pa.PA_F16))) > 0
+    i8 = _pool(d=128, dtype=pa.PA_INT8)
+    dummy = ctypes.c_void_p(4096)
+    assert lib.pa_store_kv_int8(dummy, 256, dummy, 256, pa.PA_F16, dummy, 3, dummy, dummy, None, dummy,
+                                ctypes.byref(i8), None) == 1
+    assert lib.pa_decode_int8(None, 256, 4, pa.PA_F16, None, None, None, None, ctypes.byref(i8), None, None, 1,
+                              1, 1, 0.1, None, None, None, 0, None) == 1
+    assert lib.pa_decode_int8(None, 256, 4, 9, None, None, None, None, ctypes.byref(i8), None, None, 1,
+                              1, 1, 0.1, None, None, None, 0, None) == 3
 
 
 def test_copy_blocks_host_errors():

@@ -304,38 +304,38 @@ def c1_tiny(seed=1001):
     return pre, dec
 
 
-def c2_varlen(n, seed=None, with_values=True):
+def c2_varlen(n, seed=None, with_values=True, dtype="bf16"):
     """8 sequences x n tokens (n in {32,128,256}), fresh prompts, 16/8 heads,
     d=128, bf16, block 256; 16-block pool (8 used, 8 spare), shuffled."""
     seed = {32: 2032, 128: 2128, 256: 2256}.get(n, 2000 + n) if seed is None else seed
     return make_prefill(f"c2_varlen_8x{n}", seed, [n] * 8, [0] * 8, QWEN3_HQ, QWEN3_HKV, QWEN3_D,
-                        256, "bf16", num_spare=8, with_values=with_values)
+                        256, dtype, num_spare=8, with_values=with_values)
 
 
-def c3_prefix(seed=3300, with_values=True):
+def c3_prefix(seed=3300, with_values=True, dtype="bf16"):
     """2 sequences of 300 tokens whose first 256 tokens sit in one cached block
     each; only the 44-token suffix is prefilled (q_offsets = 256)."""
     return make_prefill("c3_prefix_2x(256+44)", seed, [44, 44], [256, 256], QWEN3_HQ, QWEN3_HKV,
-                        QWEN3_D, 256, "bf16", num_spare=4, with_values=with_values)
+                        QWEN3_D, 256, dtype, num_spare=4, with_values=with_values)
 
 
-def c4_decode_layout(seed=4000):
+def c4_decode_layout(seed=4000, dtype="bf16"):
     """256 sequences, context lengths uniform in [100, 2048], block 256; the
     block table and lengths are shared by all 28 layers.  Values are drawn per
     layer (seed 4100 + layer) by the caller, on the device for timing."""
     rng = np.random.default_rng(seed)
     ctx = rng.integers(100, 2048, size=256, endpoint=True).astype(np.int32)
     return make_decode("c4_decode_256xU[100,2048]", seed, ctx, QWEN3_HQ, QWEN3_HKV, QWEN3_D, 256,
-                       "bf16", num_spare=2, with_values=False)
+                       dtype, num_spare=2, with_values=False)
 
 
-def c5a_long(seed=5096, with_values=True):
+def c5a_long(seed=5096, with_values=True, dtype="bf16"):
     """1 sequence x 4096-token causal prefill, block 16, 16 spare blocks."""
     return make_prefill("c5a_prefill_1x4096", seed, [4096], [0], QWEN3_HQ, QWEN3_HKV, QWEN3_D, 16,
-                        "bf16", num_spare=16, with_values=with_values)
+                        dtype, num_spare=16, with_values=with_values)
 
 
-def c5a_mixed(seed=5192, budget=8192, with_values=True):
+def c5a_mixed(seed=5192, budget=8192, with_values=True, dtype="bf16"):
     """Chunked-prefill batch under an 8192-token budget: prompt lengths uniform
     in [100, 1024]; sequence 0 resumes with a cached prefix uniform in
     [1, L0-1]; fresh prompts follow; the last one is cut so the new tokens
@@ -352,15 +352,25 @@ def c5a_mixed(seed=5192, budget=8192, with_values=True):
         q_offs.append(0)
     k_total_blocks = sum(-(-(a + b) // 16) for a, b in zip(q_lens, q_offs))
     return make_prefill("c5a_mixed_chunked_8192", seed + 1, q_lens, q_offs, QWEN3_HQ, QWEN3_HKV,
-                        QWEN3_D, 16, "bf16", num_spare=max(1, k_total_blocks // 20),
+                        QWEN3_D, 16, dtype, num_spare=max(1, k_total_blocks // 20),
                         with_values=with_values)
 
 
-def c5b_decode_layout(seed=5327):
+def c5b_decode_layout(seed=5327, dtype="bf16"):
     """64 sequences x 32768-token contexts, block 16 (131072 blocks + spare)."""
     ctx = np.full(64, 32768, dtype=np.int32)
-    return make_decode("c5b_decode_64x32768", seed, ctx, QWEN3_HQ, QWEN3_HKV, QWEN3_D, 16, "bf16",
+    return make_decode("c5b_decode_64x32768", seed, ctx, QWEN3_HQ, QWEN3_HKV, QWEN3_D, 16, dtype,
                        num_spare=16, with_values=False)
+
+
+def fork_microbench_decode(seed=8512, dtype="f16", block_size=256, with_values=True):
+    """The fork's fused-dequantization microbenchmark shape (LLM inference
+    interview notes (nano-vllm fork), Q3, INT8-versus-FP16 latency table):
+    batch 8, 16 query / 8 KV heads, head_dim 128, fp16.  Its cache-byte
+    column counts 512 tokens per sequence, so the 511 cached tokens plus the
+    token being decoded give 512 visible keys per row."""
+    return make_decode("fork_microbench_decode_8x512", seed, [512] * 8, QWEN3_HQ, QWEN3_HKV, QWEN3_D,
+                       block_size, dtype, num_spare=2, with_values=with_values)
 
 
 # --------------------------------------------------------------------------
