@@ -24,6 +24,9 @@ Outside the timed step, the INT8 KV cache is measured on the same shapes:
 the decode layers (bytes: every visible row's int8 codes and fp16 scale,
 K and V, once per KV head), `int8_store` times pa_store_kv_int8 of the
 4096-token prompt and `int8_prefill` pa_prefill_varlen_int8 over it.
+The fp16 legs (`f16_decode`, `f16_prefill`) run the same shapes over fp16
+pools and queries, and `fork_microbench_decode` times fp16 against INT8
+pools at the fork's microbenchmark shape (batch 8, 512 keys per row).
 """
 from __future__ import annotations
 
@@ -40,6 +43,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+MFMA_F16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16 MFMA
 
 
 def parse():
@@ -50,6 +54,7 @@ def parse():
     p.add_argument("--layers", type=int, default=28)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-int8", action="store_true", help="skip the INT8 KV-cache measurements")
+    p.add_argument("--no-f16", action="store_true", help="skip the fp16 measurements")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="also run one plain 1 GiB device copy (HBM counter calibration)")
     return p.parse_args()
@@ -181,6 +186,9 @@ def main():
                                                   pf_kn, pf_vn, pf_slots, dec_call_ms, max(args.steps, 2),
                                                   (pf_q, pf_cuq, pf_cuk, pf_off, pf_bt, pf_flops, pf_call_ms))
 
+    f16 = None if args.no_f16 else f16_measure(pa, W, lay, ctx_d, bt_d, order_d, dec_call_ms, pf_call_ms,
+                                               max(args.steps, 2))
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(lay, k_pools[0], v_pools[0], qs[0])
@@ -234,6 +242,8 @@ def main():
     }
     if int8 is not None:
         result.update(int8)
+    if f16 is not None:
+        result.update(f16)
     print(json.dumps(result), flush=True)
 
 
@@ -336,6 +346,107 @@ def int8_measure(pa, W, lay, pf, k_pools, v_pools, qs, ctx_d, bt_d, order_d, pf_
             "workload": "pa_store_kv_int8 of 4096 tokens x 8 KV heads x 128 (bf16 in, int8 + fp16 scale out)",
             "avg_launch_us": round(st_ms * 1e3, 2), "bytes_per_launch": st_bytes,
             "achieved_gbps": round(st_bytes / (st_ms * 1e-3) / 1e9, 2),
+        },
+    }
+
+
+def _time_calls(fns, reps):
+    """Mean duration (ms) of each call in fns, from HIP events on the current
+    stream, over reps rounds after two untimed rounds."""
+    import torch
+    stream = torch.cuda.current_stream()
+    for _ in range(2):
+        for fn in fns:
+            fn()
+    torch.cuda.synchronize()
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in fns]
+          for _ in range(reps)]
+    for r in range(reps):
+        for i, fn in enumerate(fns):
+            ev[r][i][0].record(stream)
+            fn()
+            ev[r][i][1].record(stream)
+    torch.cuda.synchronize()
+    return float(np.mean([a.elapsed_time(b) for row in ev for a, b in row]))
+
+
+def f16_measure(pa, W, lay, ctx_d, bt_d, order_d, bf16_dec_ms, bf16_pf_ms, reps, layers=4):
+    """fp16 pools and queries (not part of the step): the decode shape over
+    `layers` fp16 layer pools, the 1 x 4096 prefill on the fp16 matrix cores,
+    and the fork's fp16-versus-INT8 decode microbenchmark shape (batch 8,
+    16 / 8 heads, head_dim 128, 512 keys per row)."""
+    import torch
+    dev = "cuda"
+    nb, bs, hkv, d, hq = lay.num_blocks, lay.block_size, lay.num_kv_heads, lay.head_dim, lay.num_q_heads
+    pools = [(W.device_normal((nb, bs, hkv, d), 4500 + 2 * i, dtype="f16"),
+              W.device_normal((nb, bs, hkv, d), 4501 + 2 * i, dtype="f16"),
+              W.device_normal((lay.num_seqs, hq, d), 9500 + i, dtype="f16")) for i in range(layers)]
+    out = torch.empty((lay.num_seqs, hq, d), dtype=torch.float16, device=dev)
+    wsb = pa.pa_decode_workspace_bytes(lay.num_seqs, hq, lay.max_context_len, pools[0][0])
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+    dec_ms = _time_calls([lambda i=i: pa.pa_decode(pools[i][2], pools[i][0], pools[i][1], ctx_d, bt_d,
+                                                   lay.max_context_len, lay.scale, out=out, workspace=ws,
+                                                   row_order=order_d) for i in range(layers)], reps)
+    dec_bytes = lay.kv_bytes()
+    dec_gbps = dec_bytes / (dec_ms * 1e-3) / 1e9
+
+    pf = W.c5a_long(dtype="f16", with_values=False)
+    kp = W.device_normal((pf.num_blocks, pf.block_size, pf.num_kv_heads, pf.head_dim), 5300, dtype="f16")
+    vp = W.device_normal((pf.num_blocks, pf.block_size, pf.num_kv_heads, pf.head_dim), 5301, dtype="f16")
+    q = W.device_normal((pf.total_q, pf.num_q_heads, pf.head_dim), 5302, dtype="f16")
+    pf_out = torch.empty_like(q)
+    i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)  # noqa: E731
+    cuq, cuk, off, bt = i32(pf.cu_seqlens_q), i32(pf.cu_seqlens_k), i32(pf.q_offsets), i32(pf.block_table)
+    pf_ms = _time_calls([lambda: pa.pa_prefill_varlen(q, kp, vp, cuq, cuk, off, bt, pf.max_seqlen_q,
+                                                      pf.max_seqlen_k, pf.scale, out=pf_out)], reps)
+    pf_flops = 4.0 * pf.head_dim * pf.num_q_heads * pf.causal_pairs
+    pf_tflops = pf_flops / (pf_ms * 1e-3) / 1e12
+
+    mb = W.fork_microbench_decode(with_values=False)
+    mk = W.device_normal((mb.num_blocks, mb.block_size, mb.num_kv_heads, mb.head_dim), 8600, dtype="f16")
+    mv = W.device_normal((mb.num_blocks, mb.block_size, mb.num_kv_heads, mb.head_dim), 8601, dtype="f16")
+    mq = W.device_normal((mb.num_seqs, mb.num_q_heads, mb.head_dim), 8602, dtype="f16")
+    mctx, mbt = i32(mb.context_lens), i32(mb.block_table)
+    slots = torch.arange(mb.num_blocks * mb.block_size, dtype=torch.int32, device=dev)
+    shape = (mb.num_blocks, mb.block_size, mb.num_kv_heads, mb.head_dim)
+    kq, vq = torch.empty(shape, dtype=torch.int8, device=dev), torch.empty(shape, dtype=torch.int8, device=dev)
+    ks = torch.empty(shape[:3], dtype=torch.float16, device=dev)
+    vs = torch.empty_like(ks)
+    flat = (mb.num_blocks * mb.block_size, mb.num_kv_heads, mb.head_dim)
+    pa.pa_store_kv_int8(mk.view(flat), mv.view(flat), slots, kq, vq, ks, vs)
+    mout = torch.empty_like(mq)
+    mws = torch.empty(max(pa.pa_decode_workspace_bytes(mb.num_seqs, mb.num_q_heads, mb.max_context_len, mk),
+                          pa.pa_decode_int8_workspace_bytes(mb.num_seqs, mb.num_q_heads, mb.max_context_len, kq,
+                                                            ks), 1), dtype=torch.uint8, device=dev)
+    mb_f16 = _time_calls([lambda: pa.pa_decode(mq, mk, mv, mctx, mbt, mb.max_context_len, mb.scale, out=mout,
+                                               workspace=mws)], max(reps, 20))
+    mb_i8 = _time_calls([lambda: pa.pa_decode_int8(mq, kq, vq, ks, vs, mctx, mbt, mb.max_context_len, mb.scale,
+                                                   out=mout, workspace=mws)], max(reps, 20))
+    mb_tokens = int(mb.context_lens.sum()) * mb.num_kv_heads
+    return {
+        "f16_decode": {
+            "value": round(dec_gbps, 2), "unit": "GB/s",
+            "workload": f"decode 256 seqs ctx U[100,2048], fp16 pools and queries, {layers} layer pools",
+            "avg_launch_us": round(dec_ms * 1e3, 2), "bytes_per_launch": dec_bytes,
+            "time_vs_bf16_decode": round(dec_ms / bf16_dec_ms, 3),
+            "roofline": {"bound": "hbm", "achieved": round(dec_gbps, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                         "frac": round(dec_gbps / HBM_PEAK_GBPS, 4)},
+        },
+        "f16_prefill": {
+            "value": round(pf_tflops, 2), "unit": "TFLOP/s",
+            "workload": "prefill 1x4096 causal (block 16), fp16 pools and queries, fp16 MFMA",
+            "avg_launch_us": round(pf_ms * 1e3, 2), "flops_per_launch": pf_flops,
+            "time_vs_bf16_prefill": round(pf_ms / bf16_pf_ms, 3),
+            "roofline": {"bound": "mfma", "achieved": round(pf_tflops, 2), "peak": MFMA_F16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(pf_tflops / MFMA_F16_PEAK_TFLOPS, 4)},
+        },
+        "fork_microbench_decode": {
+            "workload": ("decode batch 8 x 512 keys, 16 q / 8 kv heads, head_dim 128, block 256: fp16 pools "
+                         "against INT8 pools (fp16 queries)"),
+            "f16_us": round(mb_f16 * 1e3, 2), "int8_us": round(mb_i8 * 1e3, 2),
+            "int8_over_f16_time": round(mb_i8 / mb_f16, 3),
+            "f16_cache_bytes": mb_tokens * mb.head_dim * 2 * 2,
+            "int8_cache_bytes": mb_tokens * (mb.head_dim + 2) * 2,
         },
     }
 

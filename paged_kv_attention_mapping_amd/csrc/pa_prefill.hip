@@ -1,5 +1,5 @@
 // pa_prefill.hip -- query-tiled flash-attention prefill over the paged KV
-// cache on bf16 MFMA (gfx950), for head_dim 64 and 128.
+// cache on bf16 or fp16 MFMA (gfx950), for head_dim 64 and 128.
 //
 // What it computes (nano-vllm deep dive, Step 4 path A/B, flash_attn_varlen_func
 // with cu_seqlens and block_table, causal): query i of sequence s sits at
@@ -63,8 +63,6 @@
 namespace pa {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -77,8 +75,45 @@ constexpr int kRowsPerWave = kStep / kPfWaves;  // step rows each wave loads (16
 constexpr int kBlkWin = 1024;                 // block ids staged in LDS at a time
 constexpr float kLog2eF = 1.4426950408889634f;
 
-template <int D, int NH>
+// The 16-bit element type of the pools, the queries and the matrix-core
+// operands: bf16 (v_mfma_f32_32x32x16_bf16) or IEEE fp16
+// (v_mfma_f32_32x32x16_f16), with the same 32x32x16 operand layouts.  The
+// probabilities are rounded to the same type; kBlockSumMax bounds them (see
+// attend_tile) below the type's largest finite value.
+template <typename E> struct Mm;
+template <> struct Mm<bf16_t> {
+    typedef __bf16 x8 __attribute__((ext_vector_type(8)));
+    typedef __bf16 x4 __attribute__((ext_vector_type(4)));
+    typedef __bf16 x2 __attribute__((ext_vector_type(2)));
+    // every P <= 2^20: O and l stay far inside fp32 range
+    static constexpr float kBlockSumMax = 1048576.f;
+    static __device__ __forceinline__ f32x16 mfma(const x8 &a, const x8 &b, const f32x16 &c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ float dot2(const x2 &a, const x2 &b, float c) {
+        return __builtin_amdgcn_fdot2_f32_bf16(a, b, c, false);
+    }
+};
+template <> struct Mm<f16_t> {
+    typedef _Float16 x8 __attribute__((ext_vector_type(8)));
+    typedef _Float16 x4 __attribute__((ext_vector_type(4)));
+    typedef _Float16 x2 __attribute__((ext_vector_type(2)));
+    // every P <= 2^14, inside fp16's range (largest finite 65504)
+    static constexpr float kBlockSumMax = 16384.f;
+    static __device__ __forceinline__ f32x16 mfma(const x8 &a, const x8 &b, const f32x16 &c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ float dot2(const x2 &a, const x2 &b, float c) {
+        return __builtin_amdgcn_fdot2(a, b, c, false);
+    }
+};
+
+template <int D, int NH, typename E = bf16_t>
 struct Pf {
+    using M = Mm<E>;
+    typedef typename M::x8 x8;
+    typedef typename M::x4 x4;
+    typedef typename M::x2 x2;
     static constexpr int SUB = 4 / NH;                 // position sub-tiles per workgroup
     static constexpr int BM = 32 * SUB;                // positions per workgroup tile
     static constexpr int KS = D / 16;                  // MFMA k-steps over head_dim
@@ -142,7 +177,6 @@ template <int CPR> __device__ __forceinline__ int v_slot(int r, int c) { return 
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 // Max / sum of x over lanes i and i^32 (the two 32-lane halves), in every
@@ -364,55 +398,32 @@ __device__ __forceinline__ void convert_step_i8(const unsigned char *k8, const u
 // that the PV product and the row sum (dot products with ones) see the same
 // weights.  Returns this lane's sum over its 16 keys of the block.
 template <class C>
-__device__ __forceinline__ float block_probs(const f32x16 &sacc, float c, float mc, bf16x8 &p_lo, bf16x8 &p_hi) {
-    const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
+__device__ __forceinline__ float block_probs(const f32x16 &sacc, float c, float mc, typename C::x8 &p_lo,
+                                             typename C::x8 &p_hi) {
+    const typename C::x2 ones = {1.f, 1.f};
     f32x8 lo, hi;
 #pragma unroll
     for (int jj = 0; jj < 8; ++jj) {
         lo[jj] = __builtin_amdgcn_exp2f(fmaf(sacc[jj], c, -mc));
         hi[jj] = __builtin_amdgcn_exp2f(fmaf(sacc[8 + jj], c, -mc));
     }
-    p_lo = __builtin_convertvector(lo, bf16x8);
-    p_hi = __builtin_convertvector(hi, bf16x8);
+    p_lo = __builtin_convertvector(lo, typename C::x8);
+    p_hi = __builtin_convertvector(hi, typename C::x8);
     float s0 = 0.f, s1 = 0.f;
 #pragma unroll
     for (int k = 0; k < 8; k += 2) {
-        s0 = __builtin_amdgcn_fdot2_f32_bf16((bf16x2){p_lo[k], p_lo[k + 1]}, ones, s0, false);
-        s1 = __builtin_amdgcn_fdot2_f32_bf16((bf16x2){p_hi[k], p_hi[k + 1]}, ones, s1, false);
+        s0 = C::M::dot2((typename C::x2){p_lo[k], p_lo[k + 1]}, ones, s0);
+        s1 = C::M::dot2((typename C::x2){p_hi[k], p_hi[k + 1]}, ones, s1);
     }
     return s0 + s1;
 }
-
-// O^T += V^T . P^T for the 16-key group st of the tile; V^T operands by LDS
-// transpose loads: lane (group grp = lane/16, i = lane%16) names row 16st +
-// 8hf + 4x + i/4 (x = 0, 1) at column 32dt + 16(grp&1) + 4(i&3) and receives
-// V[16st + 8hf + 4x + 0..3][32dt + lane%32].  With the 4r swizzle the address
-// is a per-lane base (one per dt) plus a constant per (st, x).
-template <class C>
-__device__ __forceinline__ void pv_group(const unsigned char *vt, const int (&vrd)[C::DT], int st, const bf16x8 &pb,
-                                         f32x16 (&o)[C::DT]) {
-#pragma unroll
-    for (int dt = 0; dt < C::DT; ++dt) {
-        i16x4 part[2];
-#pragma unroll
-        for (int x = 0; x < 2; ++x)
-            part[x] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(vt + vrd[dt] + (16 * st + 4 * x) * C::ROWB));
-        const bf16x8 va = __builtin_bit_cast(bf16x8, (i16x8){part[0][0], part[0][1], part[0][2], part[0][3],
-                                                              part[1][0], part[1][1], part[1][2], part[1][3]});
-        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, o[dt], 0, 0, 0);
-    }
-}
-
-// Largest per-lane block sum of probabilities accepted without moving the
-// reference max: every P <= 2^20, so O and l stay far inside fp32 range.
-constexpr float kBlockSumMax = 1048576.f;
 
 // Cold path of one block: move the reference max to the block max (the same
 // in both lane halves of each query column), rescale O and l, and
 // exponentiate the block again.
 template <class C>
 __device__ __forceinline__ float rebase_block(const f32x16 &sacc, f32x16 (&o)[C::DT], float &m, float &l,
-                                             float c, bf16x8 &p_lo, bf16x8 &p_hi) {
+                                             float c, typename C::x8 &p_lo, typename C::x8 &p_hi) {
     float mx = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[r]);
@@ -456,13 +467,13 @@ __device__ __forceinline__ void mask_block(f32x16 &sacc, int t, int thr) {
 // transpose reads at the lane's base vofs[dt] plus an immediate offset (see
 // the kernel for the lane mapping).
 template <class C>
-__device__ __forceinline__ bf16x8 read_vt(const unsigned char *vbuf, const int (&vofs)[C::DT], int st, int dt) {
+__device__ __forceinline__ typename C::x8 read_vt(const unsigned char *vbuf, const int (&vofs)[C::DT], int st, int dt) {
     i16x4 part[2];
 #pragma unroll
     for (int x = 0; x < 2; ++x)
         part[x] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (lds_i16x4 *)(vbuf + vofs[dt] + (16 * st + 4 * x) * C::ROWB));
-    return __builtin_bit_cast(bf16x8, (i16x8){part[0][0], part[0][1], part[0][2], part[0][3], part[1][0],
+    return __builtin_bit_cast(typename C::x8, (i16x8){part[0][0], part[0][1], part[0][2], part[0][3], part[1][0],
                                              part[1][1], part[1][2], part[1][3]});
 }
 
@@ -473,16 +484,17 @@ __device__ __forceinline__ void probs_step(const f32x16 &sacc, float c, float mc
     pf[2 * i + 1] = __builtin_amdgcn_exp2f(fmaf(sacc[2 * i + 1], c, -mc));
 }
 
-// bf16 probabilities and the lane's sum of them (see block_probs).
-__device__ __forceinline__ float probs_finish(const f32x16 &pf, bf16x8 &p_lo, bf16x8 &p_hi) {
-    const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
-    p_lo = __builtin_convertvector(__builtin_shufflevector(pf, pf, 0, 1, 2, 3, 4, 5, 6, 7), bf16x8);
-    p_hi = __builtin_convertvector(__builtin_shufflevector(pf, pf, 8, 9, 10, 11, 12, 13, 14, 15), bf16x8);
+// 16-bit probabilities and the lane's sum of them (see block_probs).
+template <class C>
+__device__ __forceinline__ float probs_finish(const f32x16 &pf, typename C::x8 &p_lo, typename C::x8 &p_hi) {
+    const typename C::x2 ones = {1.f, 1.f};
+    p_lo = __builtin_convertvector(__builtin_shufflevector(pf, pf, 0, 1, 2, 3, 4, 5, 6, 7), typename C::x8);
+    p_hi = __builtin_convertvector(__builtin_shufflevector(pf, pf, 8, 9, 10, 11, 12, 13, 14, 15), typename C::x8);
     float s0 = 0.f, s1 = 0.f;
 #pragma unroll
     for (int k = 0; k < 8; k += 2) {
-        s0 = __builtin_amdgcn_fdot2_f32_bf16((bf16x2){p_lo[k], p_lo[k + 1]}, ones, s0, false);
-        s1 = __builtin_amdgcn_fdot2_f32_bf16((bf16x2){p_hi[k], p_hi[k + 1]}, ones, s1, false);
+        s0 = C::M::dot2((typename C::x2){p_lo[k], p_lo[k + 1]}, ones, s0);
+        s1 = C::M::dot2((typename C::x2){p_hi[k], p_hi[k + 1]}, ones, s1);
     }
     return s0 + s1;
 }
@@ -514,36 +526,36 @@ struct SoftState {
 template <class C>
 __device__ __forceinline__ void attend_tile(const unsigned char *kbuf, const unsigned char *vbuf,
                                             const int (&kofs)[C::KS], const int (&vofs)[C::DT],
-                                            const bf16x8 (&qf)[C::KS], SoftState<C> &st_, bool need_mask, int thr,
+                                            const typename C::x8 (&qf)[C::KS], SoftState<C> &st_, bool need_mask, int thr,
                                             float c) {
     constexpr int NPV = 2 * C::DT;  // PV MFMAs per block
     const f32x16 zero = {};
     f32x16 sacc[2];
-    bf16x8 ka[2][C::KS];
+    typename C::x8 ka[2][C::KS];
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks)
-            ka[t][ks] = *reinterpret_cast<const bf16x8 *>(kbuf + kofs[ks] + t * 32 * C::ROWB);
+            ka[t][ks] = *reinterpret_cast<const typename C::x8 *>(kbuf + kofs[ks] + t * 32 * C::ROWB);
     __builtin_amdgcn_sched_barrier(0);
-    sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[0][0], qf[0], zero, 0, 0, 0);
+    sacc[0] = C::M::mfma(ka[0][0], qf[0], zero);
 #pragma unroll
     for (int ks = 1; ks < C::KS; ++ks)
-        sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[0][ks], qf[ks], sacc[0], 0, 0, 0);
+        sacc[0] = C::M::mfma(ka[0][ks], qf[ks], sacc[0]);
     __builtin_amdgcn_sched_barrier(0);
     if (need_mask) mask_block(sacc[0], 0, thr);
 
     // ---- block 1's QK MFMAs; block 0's probabilities
     f32x16 pf;
-    sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[1][0], qf[0], zero, 0, 0, 0);
+    sacc[1] = C::M::mfma(ka[1][0], qf[0], zero);
 #pragma unroll
     for (int ks = 1; ks < C::KS; ++ks)
-        sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[1][ks], qf[ks], sacc[1], 0, 0, 0);
+        sacc[1] = C::M::mfma(ka[1][ks], qf[ks], sacc[1]);
 #pragma unroll
     for (int i = 0; i < 8; ++i) probs_step(sacc[0], c, st_.mc, i, pf);
-    bf16x8 p0_lo, p0_hi, p1_lo, p1_hi;
-    float ls = probs_finish(pf, p0_lo, p0_hi);
-    if (__builtin_expect(!st_.m_set || __any(!(ls <= kBlockSumMax)), 0)) {
+    typename C::x8 p0_lo, p0_hi, p1_lo, p1_hi;
+    float ls = probs_finish<C>(pf, p0_lo, p0_hi);
+    if (__builtin_expect(!st_.m_set || __any(!(ls <= C::M::kBlockSumMax)), 0)) {
         ls = rebase_block<C>(sacc[0], st_.o, st_.m, st_.l, c, p0_lo, p0_hi);
         st_.m_set = true;
         st_.mc = (st_.m == -INFINITY) ? 0.f : st_.m * c;
@@ -552,21 +564,20 @@ __device__ __forceinline__ void attend_tile(const unsigned char *kbuf, const uns
     if (need_mask) mask_block(sacc[1], 1, thr);
 
     // ---- block 0's PV MFMAs, block 1's probabilities and V^T reads between them
-    bf16x8 va0[NPV], va1[NPV];
+    typename C::x8 va0[NPV], va1[NPV];
 #pragma unroll
     for (int k = 0; k < NPV; ++k) va0[k] = read_vt<C>(vbuf, vofs, k / C::DT, k % C::DT);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int k = 0; k < NPV; ++k) {
-        st_.o[k % C::DT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va0[k], k < C::DT ? p0_lo : p0_hi,
-                                                                  st_.o[k % C::DT], 0, 0, 0);
+        st_.o[k % C::DT] = C::M::mfma(va0[k], k < C::DT ? p0_lo : p0_hi, st_.o[k % C::DT]);
         va1[k] = read_vt<C>(vbuf, vofs, 2 + k / C::DT, k % C::DT);
 #pragma unroll
         for (int i = k * 8 / NPV; i < (k + 1) * 8 / NPV; ++i) probs_step(sacc[1], c, st_.mc, i, pf);
         __builtin_amdgcn_sched_barrier(0);
     }
-    ls = probs_finish(pf, p1_lo, p1_hi);
-    if (__builtin_expect(__any(!(ls <= kBlockSumMax)), 0)) {
+    ls = probs_finish<C>(pf, p1_lo, p1_hi);
+    if (__builtin_expect(__any(!(ls <= C::M::kBlockSumMax)), 0)) {
         ls = rebase_block<C>(sacc[1], st_.o, st_.m, st_.l, c, p1_lo, p1_hi);
         st_.mc = (st_.m == -INFINITY) ? 0.f : st_.m * c;
     }
@@ -575,8 +586,7 @@ __device__ __forceinline__ void attend_tile(const unsigned char *kbuf, const uns
     // ---- block 1's PV MFMAs
 #pragma unroll
     for (int k = 0; k < NPV; ++k)
-        st_.o[k % C::DT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va1[k], k < C::DT ? p1_lo : p1_hi,
-                                                                  st_.o[k % C::DT], 0, 0, 0);
+        st_.o[k % C::DT] = C::M::mfma(va1[k], k < C::DT ? p1_lo : p1_hi, st_.o[k % C::DT]);
 }
 
 // One step of a wave: the direct loads of the next step into (nk, nv), if
@@ -592,15 +602,16 @@ __device__ __forceinline__ void load_and_attend(const PfArgs &a, bool load, int 
                                                 const int *s_blk, unsigned char *__restrict__ nk,
                                                 unsigned char *__restrict__ nv, bool tile,
                                                 const unsigned char *__restrict__ cur, const int (&kofs)[C::KS],
-                                                const int (&vofs)[C::DT], const bf16x8 (&qf)[C::KS],
+                                                const int (&vofs)[C::DT], const typename C::x8 (&qf)[C::KS],
                                                 SoftState<C> &st, bool need_mask, int thr, float c) {
     if (load) load_wave_rows<C>(a, kb1, kmax, shift, bmask, win0, blk0, kv_row, kv_head, koff, voff, w, lane, s_blk, nk, nv);
     if (tile) attend_tile<C>(cur, cur, kofs, vofs, qf, st, need_mask, thr, c);
 }
 
-template <int D, int NH, bool I8>
+template <int D, int NH, bool I8, typename E>
 __global__ __launch_bounds__(kPfThreads, 1) void prefill_mfma_kernel(PfArgs a) {
-    using C = Pf<D, NH>;
+    static_assert(!I8 || std::is_same<E, bf16_t>::value, "INT8 pools dequantize to bf16");
+    using C = Pf<D, NH, E>;
     // [K, V][buffer][step rows] bf16 step buffers: every buffer and block
     // offset of an LDS read is an immediate.  bf16 pools: two buffers, the
     // next step loading while this one is computed.  INT8 pools: one bf16
@@ -709,13 +720,13 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_mfma_kernel(PfArgs a) {
         const int last_blk = kmax_wg >> shift;
 
         // the wave's queries, B operand layout: lane (n, hf), k-step ks holds d = 16ks + 8hf .. +7
-        bf16x8 qf[C::KS];
+        typename C::x8 qf[C::KS];
         {
             const uint16_t *qrow = a.q + (int64_t)(q_start + i_me) * a.q_row_stride + (int64_t)h * D;
 #pragma unroll
             for (int ks = 0; ks < C::KS; ++ks) {
                 uint4 v = row_ok ? ld16(qrow + 16 * ks + 8 * hf) : make_uint4(0, 0, 0, 0);
-                qf[ks] = __builtin_bit_cast(bf16x8, v);
+                qf[ks] = __builtin_bit_cast(typename C::x8, v);
             }
         }
         SoftState<C> sm;
@@ -831,7 +842,8 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_mfma_kernel(PfArgs a) {
                             const int r = 4 * b + a4;
                             v[a4] = (sm.o[dt][r] * a1 + merge[(dt * 16 + r) * 64 + lane] * a2) * inv;
                         }
-                        *reinterpret_cast<bf16x4 *>(orow + 32 * dt + 8 * b + 4 * hf) = __builtin_convertvector(v, bf16x4);
+                        *reinterpret_cast<typename C::x4 *>(orow + 32 * dt + 8 * b + 4 * hf) =
+                            __builtin_convertvector(v, typename C::x4);
                     }
             }
         }
@@ -839,26 +851,26 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_mfma_kernel(PfArgs a) {
     }
 }
 
-template <int D, int NH, bool I8>
+template <int D, int NH, bool I8, typename E>
 hipError_t run(const PfArgs &a, int num_seqs, int max_seqlen_q, hipStream_t stream) {
-    using C = Pf<D, NH>;
+    using C = Pf<D, NH, E>;
     PfArgs b = a;
     const int max_tiles = (max_seqlen_q + C::BM - 1) / C::BM;
     b.pairs_per_seq = (max_tiles + 1) / 2;
     b.head_groups = a.group / NH;
     const int64_t wgs = (int64_t)num_seqs * b.pairs_per_seq * b.head_groups * a.hkv;
     if (wgs == 0) return hipSuccess;
-    hipLaunchKernelGGL((prefill_mfma_kernel<D, NH, I8>), dim3((unsigned)wgs), dim3(kPfThreads), 0, stream, b);
+    hipLaunchKernelGGL((prefill_mfma_kernel<D, NH, I8, E>), dim3((unsigned)wgs), dim3(kPfThreads), 0, stream, b);
     return hipGetLastError();
 }
 
-template <int D, bool I8 = false>
+template <int D, bool I8 = false, typename E = bf16_t>
 hipError_t dispatch_nh(const PfArgs &a, int num_seqs, int max_seqlen_q, hipStream_t stream) {
     switch (a.group) {
-        case 1: return run<D, 1, I8>(a, num_seqs, max_seqlen_q, stream);
-        case 2: return run<D, 2, I8>(a, num_seqs, max_seqlen_q, stream);
-        case 4: return run<D, 4, I8>(a, num_seqs, max_seqlen_q, stream);
-        case 8: return run<D, 4, I8>(a, num_seqs, max_seqlen_q, stream);
+        case 1: return run<D, 1, I8, E>(a, num_seqs, max_seqlen_q, stream);
+        case 2: return run<D, 2, I8, E>(a, num_seqs, max_seqlen_q, stream);
+        case 4: return run<D, 4, I8, E>(a, num_seqs, max_seqlen_q, stream);
+        case 8: return run<D, 4, I8, E>(a, num_seqs, max_seqlen_q, stream);
     }
     return hipErrorInvalidValue;
 }
@@ -868,7 +880,7 @@ hipError_t dispatch_nh(const PfArgs &a, int num_seqs, int max_seqlen_q, hipStrea
 bool prefill_mfma_supported(const PoolGeom &g, int group) {
     // 16 pool rows (one wave's share of a step) must span < 2^31 bytes for
     // the 32-bit buffer offsets
-    return g.dtype == 1 && (g.d == 64 || g.d == 128) && g.block_size >= 4 &&
+    return (g.dtype == 1 || g.dtype == 3) && (g.d == 64 || g.d == 128) && g.block_size >= 4 &&
            (group == 1 || group == 2 || group == 4 || group == 8) &&
            (int64_t)g.hkv * g.d * 2 * kRowsPerWave < ((int64_t)1 << 31);
 }
@@ -896,6 +908,9 @@ hipError_t launch_prefill_mfma(const void *q, int64_t q_row_stride, int hq, cons
     a.scale_log2 = softmax_scale * kLog2eF;
     a.out = reinterpret_cast<uint16_t *>(out);
     if (max_seqlen_q <= 0) return hipSuccess;
+    if (g.dtype == 3)
+        return g.d == 128 ? dispatch_nh<128, false, f16_t>(a, num_seqs, max_seqlen_q, stream)
+                          : dispatch_nh<64, false, f16_t>(a, num_seqs, max_seqlen_q, stream);
     return g.d == 128 ? dispatch_nh<128>(a, num_seqs, max_seqlen_q, stream)
                       : dispatch_nh<64>(a, num_seqs, max_seqlen_q, stream);
 }

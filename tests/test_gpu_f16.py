@@ -196,6 +196,59 @@ def test_prefill_c5a_long_sampled_rows():
     assert err <= tol(F16)
 
 
+def test_prefill_c5a_mixed_sampled_rows():
+    case = W.c5a_mixed(dtype=F16)
+    rng = np.random.default_rng(5116)
+    cu = case.cu_seqlens_q
+    ends = np.concatenate([cu[:-1], cu[1:] - 1])
+    rows = np.unique(np.concatenate([ends, rng.choice(case.total_q, 100, replace=False)])).astype(np.int32)
+    say(f"[f16 prefill] c5a mixed {case.num_seqs} seqs, {len(rows)} sampled rows")
+    got, ref = _prefill(case, rows=rows)
+    assert max_abs_err(got, ref) <= tol(F16)
+
+
+def test_prefill_single_visible_key_rows_return_v_and_determinism():
+    """Row 0 of a fresh prompt sees key 0 only: its output is V[0] bit for bit
+    (P = 1 and l = 1 are exact in fp16); a second launch repeats every bit."""
+    case = W.make_prefill("f16_one", 890, [1, 64, 129], [0, 0, 0], 16, 8, 128, 16, F16)
+    say("[f16 prefill] single-key rows + determinism")
+    kp, vp = host_pools_with_prefix(case)
+    kd, vd = to_dev(kp), to_dev(vp)
+    _store_both(case, kp, vp, kd, vd)
+    args = (to_dev(case.cu_seqlens_q), to_dev(case.cu_seqlens_k), to_dev(np.zeros(3, np.int32)),
+            to_dev(case.block_table), case.max_seqlen_q, case.max_seqlen_k, case.scale)
+    out = pa.pa_prefill_varlen(to_dev(case.q), kd, vd, *args)
+    again = pa.pa_prefill_varlen(to_dev(case.q), kd, vd, *args)
+    torch.cuda.synchronize()
+    for s in range(3):
+        r = int(case.cu_seqlens_q[s])
+        assert (to_host_bits(out[r]) == np.repeat(case.v_new[r], 2, axis=0)).all()
+    assert to_host_bits(again).tobytes() == to_host_bits(out).tobytes()
+
+
+@pytest.mark.parametrize("direction", ["rising", "falling"])
+def test_prefill_steep_score_ramp(direction):
+    """Scores along a ramp of about 200 log2 units over 1024 keys: rising
+    scores keep pushing the probabilities past the fp16 bound (2^14 per lane
+    and block), so the rescale path runs again and again; falling scores make
+    later keys underflow against the first block."""
+    case = W.make_prefill("f16_ramp", 7150, [1024], [0], 16, 8, 128, 16, F16)
+    rng = np.random.default_rng(7151)
+    u = rng.standard_normal(128)
+    u /= np.linalg.norm(u)
+    ramp = 40.0 * np.arange(1024) / 1024.0
+    if direction == "falling":
+        ramp = ramp[::-1].copy()
+    case.q = np.broadcast_to(40.0 * u, (1024, 16, 128)).astype(np.float16)
+    case.k_new = np.broadcast_to(ramp[:, None, None] * u[None, None, :], (1024, 8, 128)).astype(np.float16)
+    say(f"[f16 prefill] steep {direction} score ramp")
+    rows = np.array([0, 1, 31, 32, 63, 64, 100, 511, 512, 767, 1000, 1023], np.int32)
+    got, ref = _prefill(case, rows=rows)
+    err = max_abs_err(got, ref)
+    say(f"  max-abs {err:.3e}")
+    assert err <= tol(F16)
+
+
 # ---------------------------------------------------------------- INT8 pools, fp16 rows and queries
 
 def _int8_pools(nb, bs, hkv, d):
