@@ -122,8 +122,9 @@ struct RowArgs {
     const int32_t *block_table;
     int bt_stride;
     int num_rows;
-    int num_splits;
-    int split_tokens;
+    int num_splits;            // split slots per row
+    int round_tokens;          // splits are whole rounds of this many keys
+    int split_cap;             // keys per split, upper bound
     float scale_log2;          // softmax_scale * log2(e)
     void *out;
     float *ws_acc;             // [rows][hq][splits][D]
@@ -132,6 +133,17 @@ struct RowArgs {
     const _Float16 *k_scale;   // INT8 pools only: [slots][hkv] fp16 scales
     const _Float16 *v_scale;
 };
+
+// Keys per split of a row with ctx keys: the row cut into at most
+// num_splits pieces of whole rounds, none longer than split_cap.  The split
+// kernel and the merge both derive a row's split length and count from its
+// own key count this way, so the split count follows each row on the device.
+// ctx must be at most num_splits * split_cap (the callers clamp it).
+__device__ __forceinline__ int split_tokens_of(int ctx, int num_splits, int round_tokens, int split_cap) {
+    const int per = (int)(((int64_t)ctx + num_splits - 1) / num_splits);
+    const int st = (per + round_tokens - 1) / round_tokens * round_tokens;
+    return min(max(st, round_tokens), split_cap);
+}
 
 // This lane's slice of one query head, kept in the form the dot product wants:
 // bf16 and fp16 stay packed (two elements per 32-bit word, consumed by
@@ -204,17 +216,18 @@ __global__ __launch_bounds__(NW * kWave) void row_attn_split(RowArgs a, Rows row
     rows.get(row, seq, ctx);
     // Never index past the table row or past the splits the launch covers.
     ctx = (int)min((int64_t)ctx, min((int64_t)a.bt_stride << a.block_shift,
-                                     (int64_t)a.num_splits * a.split_tokens));
+                                     (int64_t)a.num_splits * a.split_cap));
+    const int st = split_tokens_of(ctx, a.num_splits, a.round_tokens, a.split_cap);
 
     T *out_row = reinterpret_cast<T *>(a.out) + ((int64_t)row * hq + (int64_t)g * G) * D;
-    const int t0 = split * a.split_tokens;
-    if (t0 >= ctx) {
+    if ((int64_t)split * st >= ctx) {
         if (split == 0)  // no visible key: defined as a zero output
             for (int i = tid; i < G * D; i += kThreads) store_elem<T>(out_row + i, 0.f);
         return;
     }
-    const int t1 = min(t0 + a.split_tokens, ctx);
-    const int nsplit_row = (ctx + a.split_tokens - 1) / a.split_tokens;
+    const int t0 = split * st;
+    const int t1 = min(t0 + st, ctx);
+    const int nsplit_row = (ctx + st - 1) / st;
     const int shift = a.block_shift;
     const int bmask = (1 << shift) - 1;
     const int b0 = t0 >> shift;
@@ -405,17 +418,18 @@ __global__ __launch_bounds__(NW * kWave) void row_attn_int8(RowArgs a, Rows rows
     int seq, ctx;
     rows.get(row, seq, ctx);
     ctx = (int)min((int64_t)ctx, min((int64_t)a.bt_stride << a.block_shift,
-                                     (int64_t)a.num_splits * a.split_tokens));
+                                     (int64_t)a.num_splits * a.split_cap));
+    const int st = split_tokens_of(ctx, a.num_splits, a.round_tokens, a.split_cap);
 
     TQ *out_row = reinterpret_cast<TQ *>(a.out) + ((int64_t)row * hq + (int64_t)g * G) * D;
-    const int t0 = split * a.split_tokens;
-    if (t0 >= ctx) {
+    if ((int64_t)split * st >= ctx) {
         if (split == 0)
             for (int i = tid; i < G * D; i += kT) store_elem<TQ>(out_row + i, 0.f);
         return;
     }
-    const int t1 = min(t0 + a.split_tokens, ctx);
-    const int nsplit_row = (ctx + a.split_tokens - 1) / a.split_tokens;
+    const int t0 = split * st;
+    const int t1 = min(t0 + st, ctx);
+    const int nsplit_row = (ctx + st - 1) / st;
     const int shift = a.block_shift;
     const int bmask = (1 << shift) - 1;
     const int b0 = t0 >> shift;
@@ -635,7 +649,8 @@ struct MergeArgs {
     int num_rows;
     int hq;
     int num_splits;
-    int split_tokens;
+    int round_tokens;
+    int split_cap;
     int bt_stride;
     int block_shift;
     const float *ws_acc;
@@ -657,8 +672,9 @@ __global__ __launch_bounds__(kThreads) void row_attn_merge(MergeArgs a, Rows row
     int seq, ctx;
     rows.get(row, seq, ctx);
     ctx = (int)min((int64_t)ctx, min((int64_t)a.bt_stride << a.block_shift,
-                                     (int64_t)a.num_splits * a.split_tokens));
-    const int ns = (ctx + a.split_tokens - 1) / a.split_tokens;
+                                     (int64_t)a.num_splits * a.split_cap));
+    const int st = split_tokens_of(ctx, a.num_splits, a.round_tokens, a.split_cap);
+    const int ns = (ctx + st - 1) / st;
     if (ns <= 1) return;  // written directly by the split kernel
     const int64_t base = ((int64_t)row * a.hq + h) * a.num_splits;
     T *o = reinterpret_cast<T *>(a.out) + ((int64_t)row * a.hq + h) * D;
@@ -715,7 +731,7 @@ hipError_t run_rows(const RowArgs &a, const Rows &rows, hipStream_t stream) {
         hipLaunchKernelGGL((row_attn_split<T, D, G, NW, Rows>), dim3((unsigned)wgs), dim3(NW * kWave), 0,
                            stream, a, rows);
     if (a.num_splits > 1) {
-        MergeArgs m{a.num_rows, a.hkv * G, a.num_splits, a.split_tokens, a.bt_stride, a.block_shift,
+        MergeArgs m{a.num_rows, a.hkv * G, a.num_splits, a.round_tokens, a.split_cap, a.bt_stride, a.block_shift,
                     a.ws_acc, a.ws_m, a.ws_l, a.out};
         const int64_t waves = (int64_t)a.num_rows * a.hkv * G;
         hipLaunchKernelGGL((row_attn_merge<T, D, Rows>), dim3((unsigned)((waves + kNW - 1) / kNW)),
@@ -781,7 +797,8 @@ RowArgs make_args(const void *q, int64_t q_row_stride, int hq, const void *k_poo
     a.bt_stride = bt_stride;
     a.num_rows = plan.num_rows;
     a.num_splits = plan.num_splits;
-    a.split_tokens = plan.split_tokens;
+    a.round_tokens = plan.round_tokens;
+    a.split_cap = plan.split_cap;
     a.scale_log2 = softmax_scale * kLog2e;
     a.out = out;
     if (plan.num_splits > 1) {
@@ -811,24 +828,23 @@ RowAttnPlan plan_row_attention(int num_rows, const PoolGeom &g, int group, int m
 #ifdef PA_I8_WAVES
     if (g.dtype == 2) waves = group <= 2 ? PA_I8_WAVES : 4;
 #endif
-    RowAttnPlan p{num_rows, 1, 1, waves};
-    if (num_rows <= 0 || max_keys <= 0) return p;
     const int tpr = tokens_per_round(g.dtype, g.d, waves);
+    // A split's keys may start anywhere in a block, so it spans at most
+    // ceil(keys / block_size) + 1 blocks: keep that within the kBlkIds block
+    // ids a workgroup stages in LDS.  Whole rounds (tpr is a power of two).
+    const int64_t cap = min((int64_t)kSplitMax, (int64_t)(kBlkIds - 1) << g.block_shift) & ~(int64_t)(tpr - 1);
+    RowAttnPlan p{num_rows, 1, tpr, (int)cap, waves};
+    if (num_rows <= 0 || max_keys <= 0) return p;
+    // Split slots per row: enough (row, KV head, split) workgroups for two
+    // waves of resident workgroups, at least one round of keys per split at
+    // max_keys, and no split longer than cap.
     const int64_t slots = 256LL * 16 / waves;        // resident workgroups on 256 CUs
     const int64_t target_wgs = 2 * slots;
     const int64_t units = (int64_t)num_rows * g.hkv;
-    // a split covers at most kBlkIds blocks (LDS staging of its block ids)
-    const int64_t cap = min((int64_t)kSplitMax, (int64_t)kBlkIds << g.block_shift);
-    int64_t split = tpr;
-    while (split < max_keys && split < cap) split <<= 1;
-    split = min(split, cap);
-    auto wgs = [&](int64_t sp) { return units * ((max_keys + sp - 1) / sp); };
-    while (split > tpr && wgs(split) < target_wgs) split >>= 1;
-#ifdef PA_SPLIT_OVERRIDE
-    split = min((int64_t)PA_SPLIT_OVERRIDE, cap);
-#endif
-    p.split_tokens = (int)split;
-    p.num_splits = (int)((max_keys + split - 1) / split);
+    int64_t ns = (target_wgs + units - 1) / units;
+    ns = min(ns, ((int64_t)max_keys + tpr - 1) / tpr);
+    ns = max(ns, ((int64_t)max_keys + cap - 1) / cap);
+    p.num_splits = (int)max(ns, (int64_t)1);
     return p;
 }
 

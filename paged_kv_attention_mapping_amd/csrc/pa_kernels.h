@@ -46,12 +46,17 @@ hipError_t launch_gather_kv(const void *k_pool, const void *v_pool, const PoolGe
 // of a prefill batch is packed query token r.
 struct RowAttnPlan {
     int num_rows;
-    int num_splits;     // splits per row (grid dimension)
-    int split_tokens;   // keys per split
+    int num_splits;     // split slots per row (grid dimension)
+    int round_tokens;   // keys a workgroup takes per round; splits are whole rounds
+    int split_cap;      // most keys one split may cover (a multiple of round_tokens)
     int waves;          // waves per workgroup
 };
 
-// Splits are chosen from host sizes only, so workspace size and launch agree.
+// The number of split slots is chosen from host sizes only (rows, KV heads,
+// an upper bound of the keys per row), so workspace size and launch agree.
+// Each row's own split length is chosen on the device from its key count
+// (split_tokens_of in the kernels): a launch planned for a capacity serves
+// every shorter row, which keeps one captured graph valid for any lengths.
 RowAttnPlan plan_row_attention(int num_rows, const PoolGeom &g, int group, int max_keys);
 size_t row_attention_workspace_bytes(const RowAttnPlan &p, int hq, int d);
 
