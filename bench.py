@@ -55,6 +55,7 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-int8", action="store_true", help="skip the INT8 KV-cache measurements")
     p.add_argument("--no-f16", action="store_true", help="skip the fp16 measurements")
+    p.add_argument("--no-graph", action="store_true", help="skip the HIP graph replay measurements")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="also run one plain 1 GiB device copy (HBM counter calibration)")
     return p.parse_args()
@@ -186,6 +187,8 @@ def main():
                                                   pf_kn, pf_vn, pf_slots, dec_call_ms, max(args.steps, 2),
                                                   (pf_q, pf_cuq, pf_cuk, pf_off, pf_bt, pf_flops, pf_call_ms))
 
+    graph = None if args.no_graph else graph_measure(step, ms_per_step, max(args.steps, 2))
+
     f16 = None if args.no_f16 else f16_measure(pa, W, lay, ctx_d, bt_d, order_d, dec_call_ms, pf_call_ms,
                                                max(args.steps, 2))
 
@@ -244,6 +247,8 @@ def main():
         result.update(int8)
     if f16 is not None:
         result.update(f16)
+    if graph is not None:
+        result["graph_step"] = graph
     print(json.dumps(result), flush=True)
 
 
@@ -370,6 +375,33 @@ def _time_calls(fns, reps):
     return float(np.mean([a.elapsed_time(b) for row in ev for a, b in row]))
 
 
+def graph_measure(step, eager_ms_per_step, reps):
+    """The whole step captured once in a HIP graph (torch's CUDAGraph over the
+    current stream) and replayed: same kernels, same buffers, no host launch
+    work per kernel."""
+    import torch
+    step()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for _ in range(2):
+        g.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(reps):
+        g.replay()
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    return {"workload": "the timed step (prefill + 28 decode layers, their stores and the row order) as one graph",
+            "ms_per_step": round(ms, 4), "eager_ms_per_step": round(eager_ms_per_step, 4),
+            "graph_over_eager_time": round(ms / eager_ms_per_step, 3)}
+
+
 def f16_measure(pa, W, lay, ctx_d, bt_d, order_d, bf16_dec_ms, bf16_pf_ms, reps, layers=4):
     """fp16 pools and queries (not part of the step): the decode shape over
     `layers` fp16 layer pools, the 1 x 4096 prefill on the fp16 matrix cores,
@@ -423,6 +455,18 @@ def f16_measure(pa, W, lay, ctx_d, bt_d, order_d, bf16_dec_ms, bf16_pf_ms, reps,
     mb_i8 = _time_calls([lambda: pa.pa_decode_int8(mq, kq, vq, ks, vs, mctx, mbt, mb.max_context_len, mb.scale,
                                                    out=mout, workspace=mws)], max(reps, 20))
     mb_tokens = int(mb.context_lens.sum()) * mb.num_kv_heads
+    # the small decode as a model step would issue it: 28 calls back to back,
+    # eager and as one captured graph
+    layers28 = lambda: [pa.pa_decode(mq, mk, mv, mctx, mbt, mb.max_context_len, mb.scale, out=mout,  # noqa: E731
+                                     workspace=mws) for _ in range(28)]
+    eager28 = _time_calls([layers28], max(reps, 10)) / 28
+    layers28()
+    torch.cuda.synchronize()
+    g28 = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g28):
+        layers28()
+    torch.cuda.synchronize()
+    graph28 = _time_calls([g28.replay], max(reps, 10)) / 28
     return {
         "f16_decode": {
             "value": round(dec_gbps, 2), "unit": "GB/s",
@@ -445,6 +489,8 @@ def f16_measure(pa, W, lay, ctx_d, bt_d, order_d, bf16_dec_ms, bf16_pf_ms, reps,
                          "against INT8 pools (fp16 queries)"),
             "f16_us": round(mb_f16 * 1e3, 2), "int8_us": round(mb_i8 * 1e3, 2),
             "int8_over_f16_time": round(mb_i8 / mb_f16, 3),
+            "f16_us_per_call_28_back_to_back": round(eager28 * 1e3, 2),
+            "f16_us_per_call_28_in_graph": round(graph28 * 1e3, 2),
             "f16_cache_bytes": mb_tokens * mb.head_dim * 2 * 2,
             "int8_cache_bytes": mb_tokens * (mb.head_dim + 2) * 2,
         },

@@ -41,6 +41,14 @@ constexpr int kThreads = kNW * kWave;
 constexpr int kUnroll = 2;    // tokens per lane per round (K and V loads each)
 constexpr int kSplitMax = 1 << 20;   // keys per split, upper bound
 constexpr int kBlkIds = 4096;        // block ids a split may span (LDS staging)
+// Fewest rounds a split covers at the planned key bound.  Shorter splits
+// spread small batches over more workgroups but each then pays the fixed
+// cost of a workgroup (block ids, queries, the cross-wave reduction, its
+// partials and their merge) for little streaming: on MI355X, 16 rounds (1024
+// keys at bf16, head_dim 128) measured fastest for one row of 20000 keys
+// (51 -> 30 us), 32 rows of 1024 (32 -> 26 us) and 8 of 4096 (37 -> 32 us),
+// against 1, 2, 4, 8, 32, 64 and 128, and left the large batches unchanged.
+constexpr int kMinRoundsPerSplit = 16;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kOrderThreads = 1024;
 
@@ -836,13 +844,13 @@ RowAttnPlan plan_row_attention(int num_rows, const PoolGeom &g, int group, int m
     RowAttnPlan p{num_rows, 1, tpr, (int)cap, waves};
     if (num_rows <= 0 || max_keys <= 0) return p;
     // Split slots per row: enough (row, KV head, split) workgroups for two
-    // waves of resident workgroups, at least one round of keys per split at
-    // max_keys, and no split longer than cap.
+    // waves of resident workgroups, but at least kMinRoundsPerSplit rounds of
+    // keys per split at max_keys, and no split longer than cap.
     const int64_t slots = 256LL * 16 / waves;        // resident workgroups on 256 CUs
     const int64_t target_wgs = 2 * slots;
     const int64_t units = (int64_t)num_rows * g.hkv;
     int64_t ns = (target_wgs + units - 1) / units;
-    ns = min(ns, ((int64_t)max_keys + tpr - 1) / tpr);
+    ns = min(ns, ((int64_t)max_keys + kMinRoundsPerSplit * tpr - 1) / (kMinRoundsPerSplit * tpr));
     ns = max(ns, ((int64_t)max_keys + cap - 1) / cap);
     p.num_splits = (int)max(ns, (int64_t)1);
     return p;

@@ -25,7 +25,7 @@ from helpers import max_abs_err, say, to_dev, to_host_bits, tol
 pytestmark = pytest.mark.gpu
 
 HQ, HKV, D, BS = 16, 8, 128, 16
-B, WIDTH = 32, 64                   # decode rows, table width (blocks): 1024 keys per row
+B, WIDTH = 32, 256                  # decode rows, table width (blocks): 4096 keys per row
 PF_SEQS, PF_TOKENS, PF_MAX_Q = 3, 384, 256
 CAP_K = WIDTH * BS
 NB_DEC = B * WIDTH + 2
@@ -36,7 +36,9 @@ def _decode_case(seed):
     rng = np.random.default_rng(seed)
     ctx = rng.integers(1, CAP_K, size=B, endpoint=True).astype(np.int32)
     ctx[rng.choice(np.arange(1, B), 3, replace=False)] = 0      # padding rows
-    ctx[0] = CAP_K if seed % 2 else int(rng.integers(1, 64))    # a full row, or short rows only
+    ctx[0] = CAP_K if seed % 2 else int(rng.integers(1, 64))    # a full row, or no row past 4032 keys
+    if seed % 2 == 0:
+        ctx = np.minimum(ctx, CAP_K - 64)
     return W.make_decode("graph_dec", seed, ctx, HQ, HKV, D, BS, "bf16", num_spare=2)
 
 
