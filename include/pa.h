@@ -41,8 +41,8 @@
  * block_size a power of two (1 .. 65536); num_q_heads a multiple of
  * num_kv_heads with group size num_q_heads / num_kv_heads in {1, 2, 4, 8}.
  * Query head h reads KV head h / (num_q_heads / num_kv_heads).
- * The bf16 prefill runs on MFMA for head_dim 64 and 128; every other
- * supported shape runs on the vector ALU path.  Outputs of a 16-bit type are
+ * The bf16 and fp16 prefills run on MFMA for head_dim 64 and 128; every
+ * other supported shape runs on the vector ALU path.  Outputs of a 16-bit type are
  * the fp32 result rounded to nearest even (fp16: beyond +-65504 it is +-inf).
  */
 #ifndef PA_H
@@ -235,7 +235,9 @@ pa_status pa_copy_blocks(void *k_pool, void *v_pool, void *k_scale, void *v_scal
  *                 only the first ceil(k_len(s) / block_size) entries of a
  *                 row are read.
  *   max_seqlen_q, max_seqlen_k  host upper bounds of q_len(s) and k_len(s)
- *                 (they size the launch; no device read is needed).
+ *                 (they size the launch; no device read is needed, so a
+ *                 call captured in a HIP graph with bounds stays valid for
+ *                 any lengths within them).
  *   softmax_scale multiplies q . k before the softmax (usually 1/sqrt(d));
  *                 it must be finite and > 0 (else PA_ERR_BAD_SHAPE).
  *   out           [total_q][num_q_heads][head_dim] contiguous, `pool->dtype`
@@ -263,7 +265,13 @@ pa_status pa_prefill_varlen(const void *q, int64_t q_row_stride, int32_t num_q_h
  *   context_lens  int32 [num_seqs]; sequence s attends to keys
  *                 0 .. context_lens[s]-1.  0 marks a padding row (output 0).
  *   block_table   int32 [num_seqs][block_table_stride].
- *   max_context_len  host upper bound of context_lens (sizes the launch).
+ *   max_context_len  host upper bound of context_lens: it sizes the launch
+ *                 and the workspace; each row's split count is then chosen
+ *                 on the device from its own context length.  So a call
+ *                 captured in a HIP graph with max_context_len = the table's
+ *                 capacity (block_table_stride * block_size) stays valid for
+ *                 every context length up to it (fork Q&A, general Q&A: the
+ *                 graph-versus-kernel-choice trade-off).
  *   softmax_scale as for pa_prefill_varlen (finite, > 0).
  *   row_order     NULL, or int32 [num_seqs]: a permutation of 0..num_seqs-1
  *                 (precondition; pa_validate_decode_metadata checks a host
