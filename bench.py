@@ -345,7 +345,8 @@ def int8_measure(pa, W, lay, pf, k_pools, v_pools, qs, ctx_d, bt_d, order_d, pf_
             "avg_launch_us": round(pf_ms * 1e3, 2), "flops_per_launch": pf_flops,
             "time_vs_bf16_prefill": round(pf_ms / pf_bf16_ms, 3),
             "roofline": {"bound": "mfma", "achieved": round(pf_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
-                         "unit": "TFLOP/s", "frac": round(pf_tflops / MFMA_BF16_PEAK_TFLOPS, 4)},
+                         "unit": "TFLOP/s", "frac": round(pf_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                         "traffic": measured_traffic("prefill_int8")},
         },
         "int8_store": {
             "workload": "pa_store_kv_int8 of 4096 tokens x 8 KV heads x 128 (bf16 in, int8 + fp16 scale out)",
@@ -474,7 +475,7 @@ def f16_measure(pa, W, lay, ctx_d, bt_d, order_d, bf16_dec_ms, bf16_pf_ms, reps,
             "avg_launch_us": round(dec_ms * 1e3, 2), "bytes_per_launch": dec_bytes,
             "time_vs_bf16_decode": round(dec_ms / bf16_dec_ms, 3),
             "roofline": {"bound": "hbm", "achieved": round(dec_gbps, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                         "frac": round(dec_gbps / HBM_PEAK_GBPS, 4)},
+                         "frac": round(dec_gbps / HBM_PEAK_GBPS, 4), "traffic": measured_traffic("decode_f16")},
         },
         "f16_prefill": {
             "value": round(pf_tflops, 2), "unit": "TFLOP/s",
@@ -482,7 +483,8 @@ def f16_measure(pa, W, lay, ctx_d, bt_d, order_d, bf16_dec_ms, bf16_pf_ms, reps,
             "avg_launch_us": round(pf_ms * 1e3, 2), "flops_per_launch": pf_flops,
             "time_vs_bf16_prefill": round(pf_ms / bf16_pf_ms, 3),
             "roofline": {"bound": "mfma", "achieved": round(pf_tflops, 2), "peak": MFMA_F16_PEAK_TFLOPS,
-                         "unit": "TFLOP/s", "frac": round(pf_tflops / MFMA_F16_PEAK_TFLOPS, 4)},
+                         "unit": "TFLOP/s", "frac": round(pf_tflops / MFMA_F16_PEAK_TFLOPS, 4),
+                         "traffic": measured_traffic("prefill_f16")},
         },
         "fork_microbench_decode": {
             "workload": ("decode batch 8 x 512 keys, 16 q / 8 kv heads, head_dim 128, block 256: fp16 pools "
