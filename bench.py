@@ -434,6 +434,17 @@ def f16_measure(pa, W, lay, ctx_d, bt_d, order_d, bf16_dec_ms, bf16_pf_ms, reps,
                                                       pf.max_seqlen_k, pf.scale, out=pf_out)], reps)
     pf_flops = 4.0 * pf.head_dim * pf.num_q_heads * pf.causal_pairs
     pf_tflops = pf_flops / (pf_ms * 1e-3) / 1e12
+    # the same prefill over INT8 pools quantized from the fp16 ones, fp16 queries
+    pshape = (pf.num_blocks, pf.block_size, pf.num_kv_heads, pf.head_dim)
+    pkq, pvq = torch.empty(pshape, dtype=torch.int8, device=dev), torch.empty(pshape, dtype=torch.int8, device=dev)
+    pks = torch.empty(pshape[:3], dtype=torch.float16, device=dev)
+    pvs = torch.empty_like(pks)
+    pflat = (pf.num_blocks * pf.block_size, pf.num_kv_heads, pf.head_dim)
+    pa.pa_store_kv_int8(kp.view(pflat), vp.view(pflat),
+                        torch.arange(pflat[0], dtype=torch.int32, device=dev), pkq, pvq, pks, pvs)
+    pf8_ms = _time_calls([lambda: pa.pa_prefill_varlen_int8(q, pkq, pvq, pks, pvs, cuq, cuk, off, bt,
+                                                            pf.max_seqlen_q, pf.max_seqlen_k, pf.scale,
+                                                            out=pf_out)], reps)
 
     mb = W.fork_microbench_decode(with_values=False)
     mk = W.device_normal((mb.num_blocks, mb.block_size, mb.num_kv_heads, mb.head_dim), 8600, dtype="f16")
@@ -485,6 +496,11 @@ def f16_measure(pa, W, lay, ctx_d, bt_d, order_d, bf16_dec_ms, bf16_pf_ms, reps,
             "roofline": {"bound": "mfma", "achieved": round(pf_tflops, 2), "peak": MFMA_F16_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(pf_tflops / MFMA_F16_PEAK_TFLOPS, 4),
                          "traffic": measured_traffic("prefill_f16")},
+        },
+        "int8_prefill_f16q": {
+            "value": round(pf_flops / (pf8_ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+            "workload": "prefill 1x4096 causal over INT8 pools (block 16), fp16 queries, fp16 MFMA",
+            "avg_launch_us": round(pf8_ms * 1e3, 2), "time_vs_f16_prefill": round(pf8_ms / pf_ms, 3),
         },
         "fork_microbench_decode": {
             "workload": ("decode batch 8 x 512 keys, 16 q / 8 kv heads, head_dim 128, block 256: fp16 pools "

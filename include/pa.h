@@ -172,11 +172,12 @@ pa_status pa_decode_int8(const void *q, int64_t q_row_stride, int32_t num_q_head
  * describes for prefill).  Same arguments, semantics and errors as
  * pa_prefill_varlen, plus q_dtype (PA_BF16 / PA_F16 / PA_F32, also out's
  * type) and the fp16 scale pools; INT8 pools as for pa_decode_int8 (query
- * groups 1, 2, 4).  bf16 queries with head_dim 64 or 128, an even number of
- * KV heads, a 16-byte aligned out and 4-byte aligned scale pools run on the
- * matrix cores (each key step's codes are dequantized to bf16 in LDS); every
- * other call takes each packed query token as one row of the INT8 decode pass
- * over its visible keys (vector ALU).
+ * groups 1, 2, 4).  bf16 or fp16 queries with head_dim 64 or 128, an even
+ * number of KV heads, a 16-byte aligned out and 4-byte aligned scale pools
+ * run on the matrix cores (each key step's codes are dequantized to the query
+ * type in LDS; for fp16 they saturate at +-65504); every other call takes
+ * each packed query token as one row of the INT8 decode pass over its
+ * visible keys (vector ALU).
  */
 size_t pa_prefill_int8_workspace_bytes(int32_t num_seqs, int32_t total_q, int32_t num_q_heads,
                                        int32_t max_seqlen_k, const pa_pool *pool /* host */);

@@ -331,9 +331,10 @@ pa_status pa_prefill_varlen_int8(const void *q, int64_t q_row_stride, int32_t nu
         ((reinterpret_cast<uintptr_t>(k_scale) | reinterpret_cast<uintptr_t>(v_scale)) & 1))
         return PA_ERR_UNSUPPORTED;
     const int group = num_q_heads / g.hkv;
-    if (q_dtype == PA_BF16 && pa::prefill_mfma_int8_supported(g, group) && aligned16(out) &&
+    if ((q_dtype == PA_BF16 || q_dtype == PA_F16) && pa::prefill_mfma_int8_supported(g, group) && aligned16(out) &&
         !((reinterpret_cast<uintptr_t>(k_scale) | reinterpret_cast<uintptr_t>(v_scale)) & 3))
-        return from_hip(pa::launch_prefill_mfma_int8(q, q_row_stride, num_q_heads, k_pool, v_pool, k_scale, v_scale,
+        return from_hip(pa::launch_prefill_mfma_int8(q, q_row_stride, num_q_heads, q_dtype, k_pool, v_pool, k_scale,
+                                                     v_scale,
                                                      g, cu_seqlens_q, cu_seqlens_k, q_offsets, block_table,
                                                      block_table_stride, num_seqs, max_seqlen_q, softmax_scale, out,
                                                      (hipStream_t)stream));

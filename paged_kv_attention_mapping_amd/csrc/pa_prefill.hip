@@ -355,15 +355,17 @@ __device__ __forceinline__ void load_wave_rows_i8(const PfArgs &a, int kb_step, 
     }
 }
 
-// Dequantize one staged INT8 step into the bf16 step buffer: code * scale,
-// exact in fp32, rounded once to bf16 (nearest even), written in the same
-// swizzled layout the direct bf16 loads produce (K rows XOR r, V rows XOR 4r).
-// Codes are widened in their +128 offset form: (u - 128) s = fma(u, s, -128 s).
+// Dequantize one staged INT8 step into the 16-bit step buffer: code * scale,
+// exact in fp32, rounded once to the element type (nearest even), written in
+// the same swizzled layout the direct loads produce (K rows XOR r, V rows XOR
+// 4r).  Codes are widened in their +128 offset form: (u - 128) s =
+// fma(u, s, -128 s).  fp16: values saturate at +-65504 (127 times a scale
+// rounded up can pass fp16's largest finite value by up to 0.05%).
 template <class C>
 __device__ __forceinline__ void convert_step_i8(const unsigned char *k8, const unsigned char *v8,
                                                 const uint32_t *sk, const uint32_t *sv, int g, unsigned char *kt,
                                                 unsigned char *vt, int tid) {
-    typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+    constexpr bool kF16 = std::is_same<typename C::x8, Mm<f16_t>::x8>::value;
 #pragma unroll
     for (int t = 0; t < C::CONV; ++t) {
         const int cid = tid + kPfThreads * t;
@@ -382,13 +384,19 @@ __device__ __forceinline__ void convert_step_i8(const unsigned char *k8, const u
             for (int b = 0; b < 8; ++b) {
                 lo[b] = fmaf((float)((wd[b / 4] >> (8 * (b % 4))) & 0xffu), sc, nsc);
                 hi[b] = fmaf((float)((wd[2 + b / 4] >> (8 * (b % 4))) & 0xffu), sc, nsc);
+                if constexpr (kF16) {
+                    lo[b] = __builtin_amdgcn_fmed3f(lo[b], -65504.f, 65504.f);
+                    hi[b] = __builtin_amdgcn_fmed3f(hi[b], -65504.f, 65504.f);
+                }
             }
             const int c0 = 2 * c8;
             const int s0 = kv ? v_slot<C::CPR>(r, c0) : k_slot<C::CPR>(r, c0);
             const int s1 = kv ? v_slot<C::CPR>(r, c0 + 1) : k_slot<C::CPR>(r, c0 + 1);
             unsigned char *tile = kv ? vt : kt;
-            *reinterpret_cast<bf16x8_t *>(tile + r * C::ROWB + s0 * 16) = __builtin_convertvector(lo, bf16x8_t);
-            *reinterpret_cast<bf16x8_t *>(tile + r * C::ROWB + s1 * 16) = __builtin_convertvector(hi, bf16x8_t);
+            *reinterpret_cast<typename C::x8 *>(tile + r * C::ROWB + s0 * 16) =
+                __builtin_convertvector(lo, typename C::x8);
+            *reinterpret_cast<typename C::x8 *>(tile + r * C::ROWB + s1 * 16) =
+                __builtin_convertvector(hi, typename C::x8);
         }
     }
 }
@@ -610,7 +618,6 @@ __device__ __forceinline__ void load_and_attend(const PfArgs &a, bool load, int 
 
 template <int D, int NH, bool I8, typename E>
 __global__ __launch_bounds__(kPfThreads, 1) void prefill_mfma_kernel(PfArgs a) {
-    static_assert(!I8 || std::is_same<E, bf16_t>::value, "INT8 pools dequantize to bf16");
     using C = Pf<D, NH, E>;
     // [K, V][buffer][step rows] bf16 step buffers: every buffer and block
     // offset of an LDS read is an immediate.  bf16 pools: two buffers, the
@@ -916,13 +923,13 @@ hipError_t launch_prefill_mfma(const void *q, int64_t q_row_stride, int hq, cons
 }
 
 bool prefill_mfma_int8_supported(const PoolGeom &g, int group) {
-    // INT8 pools with bf16 queries: the scale words are 4-byte pairs of heads
+    // INT8 pools with bf16 or fp16 queries: the scale words are 4-byte pairs of heads
     // (even hkv); 16 pool rows span < 2^31 bytes
     return g.dtype == 2 && (g.d == 64 || g.d == 128) && g.block_size >= 4 && g.hkv % 2 == 0 &&
            (group == 1 || group == 2 || group == 4) && (int64_t)g.hkv * g.d * kRowsPerWave < ((int64_t)1 << 31);
 }
 
-hipError_t launch_prefill_mfma_int8(const void *q, int64_t q_row_stride, int hq, const void *k_pool,
+hipError_t launch_prefill_mfma_int8(const void *q, int64_t q_row_stride, int hq, int q_dtype, const void *k_pool,
                                     const void *v_pool, const void *k_scale, const void *v_scale, const PoolGeom &g,
                                     const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k,
                                     const int32_t *q_offsets, const int32_t *block_table, int bt_stride,
@@ -947,6 +954,9 @@ hipError_t launch_prefill_mfma_int8(const void *q, int64_t q_row_stride, int hq,
     a.scale_log2 = softmax_scale * kLog2eF;
     a.out = reinterpret_cast<uint16_t *>(out);
     if (max_seqlen_q <= 0) return hipSuccess;
+    if (q_dtype == 3)  // fp16 queries: the codes dequantize to fp16, fp16 MFMA
+        return g.d == 128 ? dispatch_nh<128, true, f16_t>(a, num_seqs, max_seqlen_q, stream)
+                          : dispatch_nh<64, true, f16_t>(a, num_seqs, max_seqlen_q, stream);
     return g.d == 128 ? dispatch_nh<128, true>(a, num_seqs, max_seqlen_q, stream)
                       : dispatch_nh<64, true>(a, num_seqs, max_seqlen_q, stream);
 }

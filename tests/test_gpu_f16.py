@@ -316,9 +316,20 @@ def test_int8_decode_fp16_queries(d, hq, hkv, bs, ctx):
     assert err <= tol(F16)
 
 
-def test_int8_prefill_fp16_queries():
-    case = W.make_prefill("i8_f16_pf", 880, [1, 67, 0, 130, 5], [0, 13, 9, 0, 250], 16, 8, 128, 16, F16)
-    say("[f16 int8 prefill] ragged 16/8 d=128 bs=16")
+INT8_F16_PREFILL = {  # name: (q_lens, q_offsets, hq, hkv, d, bs); even hkv and d 64/128 run the MFMA path
+    "ragged_16_8_d128_bs16": ([1, 67, 0, 130, 5], [0, 13, 9, 0, 250], 16, 8, 128, 16),
+    "ragged_8_2_d64_bs8": ([33, 4, 90, 200], [7, 0, 100, 31], 8, 2, 64, 8),
+    "group4_16_4_d128_bs32": ([128, 77], [0, 300], 16, 4, 128, 32),
+    "odd_hkv_rows_path_6_3_d128": ([40, 9], [5, 0], 6, 3, 128, 16),
+    "d256_rows_path": ([20, 3], [0, 11], 4, 2, 256, 16),
+}
+
+
+@pytest.mark.parametrize("name", list(INT8_F16_PREFILL))
+def test_int8_prefill_fp16_queries(name):
+    q_lens, q_offs, hq, hkv, d, bs = INT8_F16_PREFILL[name]
+    case = W.make_prefill("i8_f16_pf", 880 + d + hq + bs, q_lens, q_offs, hq, hkv, d, bs, F16)
+    say(f"[f16 int8 prefill] {name}")
     host, dev = _int8_case_pools(case)
     for k, v, s in ((case.k_cached, case.v_cached, case.slot_cached), (case.k_new, case.v_new, case.slot_new)):
         if len(s):
@@ -333,3 +344,43 @@ def test_int8_prefill_fp16_queries():
     err = max_abs_err(out, ref)
     say(f"  max-abs {err:.3e}")
     assert err <= tol(F16)
+
+
+def test_int8_prefill_fp16_queries_c5a_sampled_rows():
+    """1 x 4096 causal over INT8 pools quantized from fp16 rows, fp16 queries
+    (the fp16 matrix-core path), on sampled rows."""
+    case = W.c5a_long(dtype=F16)
+    say("[f16 int8 prefill] c5a 1x4096 sampled rows")
+    host, dev = _int8_case_pools(case)
+    pa.pa_store_kv_int8(to_dev(case.k_new), to_dev(case.v_new), to_dev(case.slot_new), *dev)
+    Q.store_kv(case.k_new, case.v_new, case.slot_new, *host)
+    offs = np.asarray(case.q_offsets, np.int32)
+    out = pa.pa_prefill_varlen_int8(to_dev(case.q), *dev, to_dev(case.cu_seqlens_q), to_dev(case.cu_seqlens_k),
+                                    to_dev(offs), to_dev(case.block_table), case.max_seqlen_q, case.max_seqlen_k,
+                                    case.scale)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([[0, 1, 4095], np.arange(4088, 4096),
+                                     np.random.default_rng(5017).choice(4096, 40, replace=False)])).astype(np.int32)
+    ref = Q.prefill(case.q, *host, case.cu_seqlens_q, case.cu_seqlens_k, offs, case.block_table, case.scale,
+                    rows=rows)
+    err = max_abs_err(out[torch.as_tensor(rows, device="cuda").long()], ref)
+    say(f"  max-abs {err:.3e}")
+    assert err <= tol(F16)
+
+
+def test_int8_prefill_fp16_saturates_at_the_largest_fp16():
+    """Rows holding +-65504: 127 times the fp16 scale (516) passes 65504, so the
+    fp16 matrix-core path saturates the dequantized values instead of making
+    them infinite; every output stays finite."""
+    case = W.make_prefill("i8_f16_sat", 881, [40], [0], 16, 8, 128, 16, F16)
+    case.k_new[3, :, 0] = np.float16(65504.0)
+    case.v_new[5, :, 1] = np.float16(-65504.0)
+    case.q[:] = (case.q.astype(np.float32) * 1e-4).astype(np.float16)
+    host, dev = _int8_case_pools(case)
+    pa.pa_store_kv_int8(to_dev(case.k_new), to_dev(case.v_new), to_dev(case.slot_new), *dev)
+    offs = np.asarray(case.q_offsets, np.int32)
+    out = pa.pa_prefill_varlen_int8(to_dev(case.q), *dev, to_dev(case.cu_seqlens_q), to_dev(case.cu_seqlens_k),
+                                    to_dev(offs), to_dev(case.block_table), case.max_seqlen_q, case.max_seqlen_k,
+                                    case.scale)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all()
