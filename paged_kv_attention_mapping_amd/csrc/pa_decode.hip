@@ -312,6 +312,9 @@ __global__ __launch_bounds__(NW * kWave) void row_attn_split(RowArgs a, Rows row
                 ps += sc[u][j];
             }
             l[j] = l[j] * alpha + ps;
+            // rescale only if the max moved for some lane of the wave (after the
+            // first rounds it seldom does; a skipped rescale is by alpha = 1)
+            if (__builtin_amdgcn_ballot_w64(alpha != 1.f))
 #pragma unroll
             for (int e = 0; e < EPV; ++e) acc[j][e] *= alpha;
         }
@@ -572,6 +575,9 @@ __global__ __launch_bounds__(NW * kWave) void row_attn_int8(RowArgs a, Rows rows
             }
             l[j] = l[j] * alpha + pl;
             ps[j] = ps[j] * alpha + pv;
+            // rescale only if the max moved for some lane of the wave (after the
+            // first rounds it seldom does; a skipped rescale is by alpha = 1)
+            if (__builtin_amdgcn_ballot_w64(alpha != 1.f))
 #pragma unroll
             for (int e = 0; e < EPV; ++e) acc[j][e] *= alpha;
         }
