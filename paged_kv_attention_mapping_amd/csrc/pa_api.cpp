@@ -336,8 +336,8 @@ pa_status pa_prefill_varlen_int8(const void *q, int64_t q_row_stride, int32_t nu
         return from_hip(pa::launch_prefill_mfma_int8(q, q_row_stride, num_q_heads, q_dtype, k_pool, v_pool, k_scale,
                                                      v_scale,
                                                      g, cu_seqlens_q, cu_seqlens_k, q_offsets, block_table,
-                                                     block_table_stride, num_seqs, max_seqlen_q, softmax_scale, out,
-                                                     (hipStream_t)stream));
+                                                     block_table_stride, num_seqs, total_q, max_seqlen_q, softmax_scale,
+                                                     out, (hipStream_t)stream));
     const pa::RowAttnPlan plan = pa::plan_row_attention(total_q, g, group, max_seqlen_k);
     const size_t need = pa::row_attention_workspace_bytes(plan, num_q_heads, g.d);
     if (need && (!workspace || workspace_bytes < need)) return PA_ERR_WORKSPACE;

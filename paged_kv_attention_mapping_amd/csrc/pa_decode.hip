@@ -69,7 +69,14 @@ struct RowCfg {
 struct DecodeRows {
     const int32_t *context_lens;
     const int32_t *order;
-    __device__ __forceinline__ int row_of(int slot) const { return order ? order[slot] : slot; }
+    int num_rows;
+    // an entry of order outside [0, num_rows) (not a permutation: a broken
+    // precondition) falls back to the slot itself, so no row is out of bounds
+    __device__ __forceinline__ int row_of(int slot) const {
+        if (!order) return slot;
+        const int r = order[slot];
+        return (unsigned)r < (unsigned)num_rows ? r : slot;
+    }
     __device__ __forceinline__ void get(int r, int &seq, int &ctx) const {
         seq = r;
         ctx = context_lens[r];
@@ -875,7 +882,7 @@ hipError_t launch_decode(const void *q, int64_t q_row_stride, int hq, const void
                          hipStream_t stream) {
     const RowArgs a = make_args(q, q_row_stride, hq, k_pool, v_pool, g, block_table, bt_stride, plan,
                                 softmax_scale, out, workspace);
-    return dispatch(g, hq / g.hkv, plan.waves, a, DecodeRows{context_lens, row_order}, stream);
+    return dispatch(g, hq / g.hkv, plan.waves, a, DecodeRows{context_lens, row_order, plan.num_rows}, stream);
 }
 
 hipError_t launch_decode_int8(const void *q, int64_t q_row_stride, int hq, int q_dtype, const void *k_pool,
@@ -887,7 +894,7 @@ hipError_t launch_decode_int8(const void *q, int64_t q_row_stride, int hq, int q
                           out, workspace);
     a.k_scale = reinterpret_cast<const _Float16 *>(k_scale);
     a.v_scale = reinterpret_cast<const _Float16 *>(v_scale);
-    const DecodeRows rows{context_lens, row_order};
+    const DecodeRows rows{context_lens, row_order, plan.num_rows};
     const int group = hq / g.hkv;
     if (q_dtype == 0) return dispatch_dim<float, DecodeRows, true>(g.d, group, plan.waves, a, rows, stream);
     if (q_dtype == 3) return dispatch_dim<f16_t, DecodeRows, true>(g.d, group, plan.waves, a, rows, stream);

@@ -82,7 +82,7 @@ hipError_t launch_prefill_mfma_int8(const void *q, int64_t q_row_stride, int hq,
                                     const void *v_pool, const void *k_scale, const void *v_scale, const PoolGeom &g,
                                     const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k,
                                     const int32_t *q_offsets, const int32_t *block_table, int bt_stride,
-                                    int num_seqs, int max_seqlen_q, float softmax_scale, void *out,
+                                    int num_seqs, int total_q, int max_seqlen_q, float softmax_scale, void *out,
                                     hipStream_t stream);
 
 // Prefill over INT8 pools, one packed query token per row.

@@ -158,6 +158,7 @@ struct PfArgs {
     const int32_t *cu_k;
     const int32_t *q_off;
     int pairs_per_seq;
+    int total_q;            // rows of q and out: packed rows past it are never touched
     float scale_log2;
     uint16_t *out;
     const uint16_t *k_scale;   // INT8 pools: fp16 scales [slots][hkv]
@@ -651,8 +652,9 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_mfma_kernel(PfArgs a) {
     const int pair = (int)(wg % a.pairs_per_seq);
     const int s = (int)(wg / a.pairs_per_seq);
 
-    const int q_start = a.cu_q[s];
-    const int q_len = a.cu_q[s + 1] - q_start;
+    // rows outside [0, total_q) are never read or written, whatever cu_seqlens_q holds
+    const int q_start = min(max(a.cu_q[s], 0), a.total_q);
+    const int q_len = min(max(a.cu_q[s + 1], 0), a.total_q) - q_start;
     const int k_len = a.cu_k[s + 1] - a.cu_k[s];
     const int q_off = a.q_off[s];
     const int T = (q_len + C::BM - 1) / C::BM;
@@ -897,8 +899,8 @@ hipError_t launch_prefill_mfma(const void *q, int64_t q_row_stride, int hq, cons
                                const int32_t *cu_seqlens_k, const int32_t *q_offsets,
                                const int32_t *block_table, int bt_stride, int num_seqs, int total_q,
                                int max_seqlen_q, float softmax_scale, void *out, hipStream_t stream) {
-    (void)total_q;
     PfArgs a{};
+    a.total_q = total_q;
     a.q = reinterpret_cast<const uint16_t *>(q);
     a.q_row_stride = q_row_stride;
     a.k_pool = reinterpret_cast<const uint16_t *>(k_pool);
@@ -933,9 +935,10 @@ hipError_t launch_prefill_mfma_int8(const void *q, int64_t q_row_stride, int hq,
                                     const void *v_pool, const void *k_scale, const void *v_scale, const PoolGeom &g,
                                     const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k,
                                     const int32_t *q_offsets, const int32_t *block_table, int bt_stride,
-                                    int num_seqs, int max_seqlen_q, float softmax_scale, void *out,
+                                    int num_seqs, int total_q, int max_seqlen_q, float softmax_scale, void *out,
                                     hipStream_t stream) {
     PfArgs a{};
+    a.total_q = total_q;
     a.q = reinterpret_cast<const uint16_t *>(q);
     a.q_row_stride = q_row_stride;
     a.k_pool = reinterpret_cast<const uint16_t *>(k_pool);

@@ -68,7 +68,7 @@ __global__ __launch_bounds__(kStoreThreads) void gather_kv_vec16(
         if (cu_seqlens_k[mid] <= row) lo = mid; else hi = mid;
     }
     const int64_t j = row - cu_seqlens_k[lo];
-    if ((j >> block_shift) >= bt_stride) return;
+    if (j < 0 || (j >> block_shift) >= bt_stride) return;  // cu_seqlens_k not covering this row
     const int64_t blk = block_table[(int64_t)lo * bt_stride + (j >> block_shift)];
     if (blk < 0 || blk >= num_blocks) return;
     const int64_t slot = (blk << block_shift) + (j & ((1 << block_shift) - 1));

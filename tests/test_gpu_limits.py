@@ -1,8 +1,8 @@
 """Limits of the supported shapes on the GPU, against the fp64 oracle: the
 largest block size (65536 tokens per block, contexts across block
 boundaries), the widest head with the largest group (d 256, 8 query heads per
-KV head), a decode batch of 4096 rows (more than a row order covers), and
-empty batches."""
+KV head), a decode batch of 4096 rows (more than a row order covers),
+empty batches, and broken metadata kept inside the buffers."""
 import numpy as np
 import pytest
 import torch
@@ -113,3 +113,49 @@ def test_empty_batches_are_no_ops():
     sentinel = torch.full((0, 16, 128), 7.0, dtype=torch.bfloat16, device="cuda")
     pa.pa_prefill_varlen(q0, kd, vd, i32(0, 0), i32(0, 5), i32(5), i32(0).view(1, 1), 0, 5, 0.1, out=sentinel)
     torch.cuda.synchronize()
+
+
+def test_broken_metadata_stays_inside_the_buffers():
+    """Broken preconditions give wrong numbers, never accesses outside the
+    buffers: cu_seqlens_q past total_q (MFMA prefill), row_order entries
+    outside [0, num_seqs) (decode), cu_seqlens_k that skip rows (gather).
+    Each output is a prefix of a larger tensor whose tail must keep its
+    canary bits."""
+    case = W.make_prefill("broken", 9430, [50, 50], [0, 7], 16, 8, 128, 16, "bf16")
+    kp, vp = host_pools_with_prefix(case)
+    kd, vd = to_dev(kp), to_dev(vp)
+    pa.pa_store_kv(to_dev(case.k_new), to_dev(case.v_new), to_dev(case.slot_new), kd, vd)
+    canary = -4096.0                                             # exact in bf16
+    big = torch.full((case.total_q + 64, 16, 128), canary, dtype=torch.bfloat16, device="cuda")
+    cu_q = np.array([0, 50, 10 ** 6], np.int32)                  # claims rows far past total_q = 100
+    pa.pa_prefill_varlen(to_dev(case.q), kd, vd, to_dev(cu_q), to_dev(case.cu_seqlens_k),
+                         to_dev(np.asarray(case.q_offsets, np.int32)), to_dev(case.block_table), 64,
+                         case.max_seqlen_k, case.scale, out=big[:case.total_q])
+    dec = W.make_decode("broken_dec", 9431, [5, 40, 300, 17, 0, 64, 1, 90], 16, 8, 128, 16, "bf16")
+    dk, dv = dec.empty_pools()
+    oracle.store_kv(dec.k_hist, dec.v_hist, dec.slot_hist, dk, dv)
+    oracle.store_kv(dec.k_new, dec.v_new, dec.slot_new, dk, dv)
+    dbig = torch.full((dec.num_seqs + 16, 16, 128), canary, dtype=torch.bfloat16, device="cuda")
+    order = np.array([3, 99, -3, 0, 7, 2 ** 31 - 1, 1, 5], np.int32)
+    pa.pa_decode(to_dev(dec.q), to_dev(dk), to_dev(dv), to_dev(dec.context_lens), to_dev(dec.block_table),
+                 dec.max_context_len, dec.scale, out=dbig[:dec.num_seqs], row_order=to_dev(order))
+    gbig = torch.full((40 + 16, 8, 128), canary, dtype=torch.bfloat16, device="cuda")
+    vbig = gbig.clone()
+    cu_k = np.array([5, 30, 12], np.int32)                       # rows 0..4 before the first sequence
+    lib = pa.load()
+    import ctypes
+    pool = pa.pool_desc(kd)
+    bt = to_dev(case.block_table)
+    cu_k_d = to_dev(cu_k)
+    code = lib.pa_gather_kv(kd.data_ptr(), vd.data_ptr(), ctypes.byref(pool), cu_k_d.data_ptr(), bt.data_ptr(),
+                            bt.shape[1], 2, 40, gbig.data_ptr(), vbig.data_ptr(),
+                            torch.cuda.current_stream().cuda_stream)
+    assert code == 0
+    torch.cuda.synchronize()
+    assert (big[case.total_q:].float() == canary).all(), "prefill wrote past total_q"
+    assert (dbig[dec.num_seqs:].float() == canary).all(), "decode wrote past num_seqs"
+    assert (gbig[40:].float() == canary).all() and (vbig[40:].float() == canary).all(), "gather wrote past total_k"
+    assert (gbig[:5].float() == canary).all(), "gather wrote rows no sequence owns"
+    # rows the order still names exactly are right
+    ref = oracle.decode(dec.q, dk, dv, dec.context_lens, dec.block_table, dec.scale, seqs=np.array([0, 3], np.int32))
+    assert max_abs_err(dbig[torch.tensor([0, 3], device="cuda")], ref) <= tol("bf16")
