@@ -202,3 +202,20 @@ def test_table_padding_is_never_read(pad):
                                  case.max_seqlen_k, case.scale)
     torch.cuda.synchronize()
     assert to_host_bits(again).tobytes() == to_host_bits(base).tobytes()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_mixed_decode_rows_and_chunks_in_one_launch(dtype):
+    """A mixed batch in one pa_prefill_varlen launch: 24 decode rows (one new
+    token after contexts of up to 2000 keys) beside 2 prefill chunks, as a
+    decode-first scheduler packs them (fork Q&A, Q2: shared token budget)."""
+    rng = np.random.default_rng(7500)
+    ctx = rng.integers(1, 2000, size=24)
+    q_lens = [1] * 24 + [300, 77]
+    q_offs = [int(c) for c in ctx] + [0, 512]
+    case = W.make_prefill("mixed", 7500, q_lens, q_offs, 16, 8, 128, 16, dtype)
+    say(f"[prefill] mixed batch: 24 decode rows + 2 chunks, {dtype}")
+    got, ref, _ = run_prefill(case)
+    err = max_abs_err(got, ref)
+    say(f"  max-abs {err:.3e}")
+    assert err <= tol(dtype)
