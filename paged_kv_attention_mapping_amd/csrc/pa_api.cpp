@@ -244,7 +244,7 @@ pa_status pa_decode(const void *q, int64_t q_row_stride, int32_t num_q_heads, co
                                       out, workspace, (hipStream_t)stream));
 }
 
-// INT8 decode: the bf16/fp32 decode's checks, with int8 code pools, fp16 scale
+// INT8 decode: the float decode's checks, with int8 code pools, fp16 scale
 // pools and q / out of q_dtype; query groups of 1, 2 or 4.
 pa_status check_decode_int8_shape(const pa_pool *pool, int32_t num_q_heads, int32_t q_dtype, pa::PoolGeom *g) {
     pa_status st = check_pool_int8(pool, g);
@@ -301,8 +301,9 @@ size_t pa_prefill_int8_workspace_bytes(int32_t num_seqs, int32_t total_q, int32_
     pa::PoolGeom g;
     if (check_decode_int8_shape(pool, num_q_heads, PA_BF16, &g) != PA_OK) return 0;
     if (num_seqs <= 0 || total_q <= 0 || max_seqlen_k <= 0) return 0;
-    // the row path's split partials (the MFMA path with bf16 queries needs none;
-    // an fp32-query call takes the row path, so the size covers it)
+    // the row path's split partials (the MFMA path for bf16 and fp16 queries
+    // needs none; fp32 queries and unsupported shapes take the row path, so
+    // the size covers it)
     const pa::RowAttnPlan plan = pa::plan_row_attention(total_q, g, num_q_heads / g.hkv, max_seqlen_k);
     return pa::row_attention_workspace_bytes(plan, num_q_heads, g.d);
 }

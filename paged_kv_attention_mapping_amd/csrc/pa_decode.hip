@@ -408,11 +408,11 @@ __global__ __launch_bounds__(NW * kWave) void row_attn_split(RowArgs a, Rows row
 // unscaled p):
 //     s_t = k_scale_t * sum_i q_i k_code_ti,   acc += (p_t * v_scale_t) * v_code_t.
 // Codes are used in their offset form u = code + 128 (one XOR per 4 codes).
-// K, with bf16 queries: a byte permute turns two codes into the fp16 pair
-// (1024 + u0, 1024 + u1), exact integers, and v_dot2_f32_f16 takes them
-// against the queries converted to fp16 (exact for bf16 values inside
-// fp16's range); the dot is sum q (1152 + code) - 1152 sum q.  fp32 queries
-// use fp32 products of the widened u.  V: u widened to fp32, and the
+// K, with bf16 or fp16 queries: a byte permute turns two codes into the fp16
+// pair (1024 + u0, 1024 + u1), exact integers, and v_dot2_f32_f16 takes them
+// against the queries in fp16 (exact for bf16 values inside fp16's range);
+// the dot is sum q (1152 + code) - 1152 sum q.  fp32 queries use fp32
+// products of the widened u.  V: u widened to fp32, and the
 // accumulator subtracts 128 * sum of the folded p at the end.
 template <typename TQ, int D, int G, int NW, class Rows>
 __global__ __launch_bounds__(NW * kWave) void row_attn_int8(RowArgs a, Rows rows) {
