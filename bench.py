@@ -24,6 +24,7 @@ Outside the timed step, the INT8 KV cache is measured on the same shapes:
 the decode layers (bytes: every visible row's int8 codes and fp16 scale,
 K and V, once per KV head), `int8_store` times pa_store_kv_int8 of the
 4096-token prompt and `int8_prefill` pa_prefill_varlen_int8 over it.
+`prefill_mixed` times the 8192-token chunked-prefill batch in one call.
 The fp16 legs (`f16_decode`, `f16_prefill`) run the same shapes over fp16
 pools and queries, and `fork_microbench_decode` times fp16 against INT8
 pools at the fork's microbenchmark shape (batch 8, 512 keys per row).
@@ -188,6 +189,7 @@ def main():
                                                   (pf_q, pf_cuq, pf_cuk, pf_off, pf_bt, pf_flops, pf_call_ms))
 
     graph = None if args.no_graph else graph_measure(step, ms_per_step, max(args.steps, 2))
+    mixed = mixed_prefill_measure(pa, W, max(args.steps, 2))
 
     f16 = None if args.no_f16 else f16_measure(pa, W, lay, ctx_d, bt_d, order_d, dec_call_ms, pf_call_ms,
                                                max(args.steps, 2))
@@ -249,6 +251,7 @@ def main():
         result.update(f16)
     if graph is not None:
         result["graph_step"] = graph
+    result["prefill_mixed"] = mixed
     print(json.dumps(result), flush=True)
 
 
@@ -374,6 +377,30 @@ def _time_calls(fns, reps):
             ev[r][i][1].record(stream)
     torch.cuda.synchronize()
     return float(np.mean([a.elapsed_time(b) for row in ev for a, b in row]))
+
+
+def mixed_prefill_measure(pa, W, reps):
+    """The chunked-prefill batch (8192 new tokens: one sequence resuming after
+    a cached prefix, then fresh prompts of U[100, 1024] tokens, block 16) in
+    one pa_prefill_varlen call, bf16 (not part of the step)."""
+    import torch
+    dev = "cuda"
+    mx = W.c5a_mixed(with_values=False)
+    shape = (mx.num_blocks, mx.block_size, mx.num_kv_heads, mx.head_dim)
+    kp, vp = W.device_normal(shape, 5400), W.device_normal(shape, 5401)
+    q = W.device_normal((mx.total_q, mx.num_q_heads, mx.head_dim), 5402)
+    out = torch.empty_like(q)
+    i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)  # noqa: E731
+    args = (i32(mx.cu_seqlens_q), i32(mx.cu_seqlens_k), i32(mx.q_offsets), i32(mx.block_table))
+    ms = _time_calls([lambda: pa.pa_prefill_varlen(q, kp, vp, *args, mx.max_seqlen_q, mx.max_seqlen_k, mx.scale,
+                                                   out=out)], reps)
+    flops = 4.0 * mx.head_dim * mx.num_q_heads * mx.causal_pairs
+    tflops = flops / (ms * 1e-3) / 1e12
+    return {"value": round(tflops, 2), "unit": "TFLOP/s",
+            "workload": f"chunked prefill batch: {mx.num_seqs} sequences, {mx.total_q} new tokens, block 16, bf16",
+            "avg_launch_us": round(ms * 1e3, 2), "flops_per_launch": flops,
+            "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)}}
 
 
 def graph_measure(step, eager_ms_per_step, reps):
