@@ -152,8 +152,9 @@ pa_status pa_store_kv_int8(const void *k, int64_t k_row_stride,
  *                 scale pools (layout above); pool->dtype PA_INT8.
  *   everything else as pa_decode (context_lens, block_table, row_order,
  *                 workspace from pa_decode_int8_workspace_bytes).
- * Query groups (num_q_heads / num_kv_heads) of 1, 2 or 4; head_dim 32, 64,
- * 128 or 256 (else PA_ERR_UNSUPPORTED).  Errors as pa_decode.
+ * Query groups (num_q_heads / num_kv_heads) of 1, 2, 4 or 8 (a group of 8
+ * reads each K/V byte twice, once per half of its query heads); head_dim 32,
+ * 64, 128 or 256 (else PA_ERR_UNSUPPORTED).  Errors as pa_decode.
  */
 size_t pa_decode_int8_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
                                       int32_t max_context_len, const pa_pool *pool /* host */);
@@ -172,9 +173,9 @@ pa_status pa_decode_int8(const void *q, int64_t q_row_stride, int32_t num_q_head
  * describes for prefill).  Same arguments, semantics and errors as
  * pa_prefill_varlen, plus q_dtype (PA_BF16 / PA_F16 / PA_F32, also out's
  * type) and the fp16 scale pools; INT8 pools as for pa_decode_int8 (query
- * groups 1, 2, 4).  bf16 or fp16 queries with head_dim 64 or 128, an even
- * number of KV heads, a 16-byte aligned out and 4-byte aligned scale pools
- * run on the matrix cores (each key step's codes are dequantized to the query
+ * groups 1, 2, 4, 8).  bf16 or fp16 queries with head_dim 64 or 128, an even
+ * number of KV heads, a group of 1, 2 or 4, a 16-byte aligned out and 4-byte
+ * aligned scale pools run on the matrix cores (each key step's codes are dequantized to the query
  * type in LDS; for fp16 they saturate at +-65504); every other call takes
  * each packed query token as one row of the INT8 decode pass over its
  * visible keys (vector ALU).

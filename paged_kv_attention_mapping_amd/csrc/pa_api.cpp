@@ -245,14 +245,14 @@ pa_status pa_decode(const void *q, int64_t q_row_stride, int32_t num_q_heads, co
 }
 
 // INT8 decode: the float decode's checks, with int8 code pools, fp16 scale
-// pools and q / out of q_dtype; query groups of 1, 2 or 4.
+// pools and q / out of q_dtype; query groups of 1, 2, 4 or 8.
 pa_status check_decode_int8_shape(const pa_pool *pool, int32_t num_q_heads, int32_t q_dtype, pa::PoolGeom *g) {
     pa_status st = check_pool_int8(pool, g);
     if (st != PA_OK) return st;
     if (!float_dtype(q_dtype)) return PA_ERR_BAD_DTYPE;
     if (num_q_heads <= 0 || num_q_heads % g->hkv) return PA_ERR_BAD_SHAPE;
     const int group = num_q_heads / g->hkv;
-    if (group != 1 && group != 2 && group != 4) return PA_ERR_UNSUPPORTED;
+    if (group != 1 && group != 2 && group != 4 && group != 8) return PA_ERR_UNSUPPORTED;
     if (g->d != 32 && g->d != 64 && g->d != 128 && g->d != 256) return PA_ERR_UNSUPPORTED;
     if (g->num_blocks < 1) return PA_ERR_BAD_SHAPE;
     return PA_OK;

@@ -147,6 +147,7 @@ struct RowArgs {
     float *ws_l;
     const _Float16 *k_scale;   // INT8 pools only: [slots][hkv] fp16 scales
     const _Float16 *v_scale;
+    int kv_shift;              // INT8 only: hkv counts 2^kv_shift virtual heads per pool head
 };
 
 // Keys per split of a row with ctx keys: the row cut into at most
@@ -426,10 +427,16 @@ __global__ __launch_bounds__(NW * kWave) void row_attn_int8(RowArgs a, Rows rows
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1), w = tid >> 6;
     const int tg = lane / LPT, c = lane % LPT;
+    // g indexes the G query heads this workgroup serves (a "virtual" KV head);
+    // gp = g >> kv_shift is the pool's KV head they read (groups of 8 run as
+    // two virtual heads of 4 query heads each, which keeps the per-lane
+    // state within the 4-wave register budget)
     const int hkv = a.hkv, hq = hkv * G;
+    const int hkv_p = hkv >> a.kv_shift;
 
     const int64_t wg = blockIdx.x;
     const int g = (int)(wg % hkv);
+    const int gp = g >> a.kv_shift;
     const int64_t rest = wg / hkv;
     const int split = (int)(rest % a.num_splits);
     const int row = rows.row_of((int)(rest / a.num_splits));
@@ -490,8 +497,8 @@ __global__ __launch_bounds__(NW * kWave) void row_attn_int8(RowArgs a, Rows rows
 
     const int8_t *kp = reinterpret_cast<const int8_t *>(a.k_pool);
     const int8_t *vp = reinterpret_cast<const int8_t *>(a.v_pool);
-    const int64_t head_off = (int64_t)g * D + c * EPV;
-    const int64_t slot_stride = (int64_t)hkv * D;
+    const int64_t head_off = (int64_t)gp * D + c * EPV;
+    const int64_t slot_stride = (int64_t)hkv_p * D;
 
     float m[G], l[G], ps[G], acc[G][EPV];
 #pragma unroll
@@ -524,8 +531,8 @@ __global__ __launch_bounds__(NW * kWave) void row_attn_int8(RowArgs a, Rows rows
             const int64_t slot = blk[u] >= 0 ? ((int64_t)blk[u] << shift) + (tok & bmask) : 0;
             kr[u] = ld16_stream(kp + slot * slot_stride + head_off);
             vr[u] = ld16_stream(vp + slot * slot_stride + head_off);
-            ks[u] = (float)a.k_scale[slot * hkv + g];
-            vs[u] = (float)a.v_scale[slot * hkv + g];
+            ks[u] = (float)a.k_scale[slot * hkv_p + gp];
+            vs[u] = (float)a.v_scale[slot * hkv_p + gp];
         }
     };
     auto consume = [&](const uint4 (&kr)[kUnroll], const uint4 (&vr)[kUnroll], const float (&ks)[kUnroll],
@@ -895,7 +902,12 @@ hipError_t launch_decode_int8(const void *q, int64_t q_row_stride, int hq, int q
     a.k_scale = reinterpret_cast<const _Float16 *>(k_scale);
     a.v_scale = reinterpret_cast<const _Float16 *>(v_scale);
     const DecodeRows rows{context_lens, row_order, plan.num_rows};
-    const int group = hq / g.hkv;
+    int group = hq / g.hkv;
+    if (group == 8) {  // two virtual KV heads of 4 query heads each per pool head
+        a.hkv = g.hkv * 2;
+        a.kv_shift = 1;
+        group = 4;
+    }
     if (q_dtype == 0) return dispatch_dim<float, DecodeRows, true>(g.d, group, plan.waves, a, rows, stream);
     if (q_dtype == 3) return dispatch_dim<f16_t, DecodeRows, true>(g.d, group, plan.waves, a, rows, stream);
     return dispatch_dim<bf16_t, DecodeRows, true>(g.d, group, plan.waves, a, rows, stream);
@@ -933,7 +945,12 @@ hipError_t launch_prefill_rows_int8(const void *q, int64_t q_row_stride, int hq,
     a.k_scale = reinterpret_cast<const _Float16 *>(k_scale);
     a.v_scale = reinterpret_cast<const _Float16 *>(v_scale);
     const PrefillRows rows{cu_seqlens_q, cu_seqlens_k, q_offsets, num_seqs};
-    const int group = hq / g.hkv;
+    int group = hq / g.hkv;
+    if (group == 8) {  // two virtual KV heads of 4 query heads each per pool head
+        a.hkv = g.hkv * 2;
+        a.kv_shift = 1;
+        group = 4;
+    }
     if (q_dtype == 0) return dispatch_dim<float, PrefillRows, true>(g.d, group, plan.waves, a, rows, stream);
     if (q_dtype == 3) return dispatch_dim<f16_t, PrefillRows, true>(g.d, group, plan.waves, a, rows, stream);
     return dispatch_dim<bf16_t, PrefillRows, true>(g.d, group, plan.waves, a, rows, stream);

@@ -67,7 +67,8 @@ hipError_t launch_decode(const void *q, int64_t q_row_stride, int hq, const void
                          hipStream_t stream);
 
 // Decode over INT8 pools (int8 codes, fp16 scales per (token, KV head));
-// q and out are q_dtype (0 fp32, 1 bf16, 3 fp16); query groups of 1, 2 or 4.
+// q and out are q_dtype (0 fp32, 1 bf16, 3 fp16); query groups of 1, 2, 4 or
+// 8 (8 runs as two virtual KV heads of 4 query heads per pool head).
 hipError_t launch_decode_int8(const void *q, int64_t q_row_stride, int hq, int q_dtype, const void *k_pool,
                               const void *v_pool, const void *k_scale, const void *v_scale, const PoolGeom &g,
                               const int32_t *context_lens, const int32_t *block_table, int bt_stride,

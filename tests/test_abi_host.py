@@ -62,8 +62,9 @@ def test_int8_store_host_errors():
 
 
 def test_int8_decode_host_errors_and_workspace():
-    """pa_decode_int8 takes PA_INT8 pools, q of bf16 / fp32, query groups of
-    1, 2 or 4; its workspace follows the same split plan as pa_decode."""
+    """pa_decode_int8 takes PA_INT8 pools, q of bf16 / fp16 / fp32, query
+    groups of 1, 2, 4 or 8; its workspace follows the same split plan as
+    pa_decode."""
     lib = pa.load()
     dummy = ctypes.c_void_p(4096)
     i8 = _pool(nb=64, bs=16, hkv=8, d=128, dtype=pa.PA_INT8)
@@ -72,7 +73,7 @@ def test_int8_decode_host_errors_and_workspace():
                                   dummy, dummy, 8, n, max_ctx, scale, None, dummy, ws, wsb, None)
     assert call(_pool(nb=64, bs=16, hkv=8, d=128, dtype=pa.PA_BF16)) == 3   # pool not INT8
     assert call(i8, qd=pa.PA_INT8) == 3                                      # q must be bf16 / fp32
-    assert call(i8, hq=64) == 4                                              # group 8 not built for INT8
+    assert call(i8, hq=128) == 4                                             # group 16 is not built
     assert call(i8, hq=12) == 2                                              # not a multiple of Hkv
     assert call(i8, scale=0.0) == 2
     assert call(i8, n=0) == 0
@@ -94,7 +95,7 @@ def test_int8_prefill_host_errors():
                                           dummy, dummy, dummy, dummy, 8, n, tq, 5, 5, scale, dummy, None, 0, None)
     assert call(_pool(nb=64, bs=16, hkv=8, d=128, dtype=pa.PA_BF16)) == 3
     assert call(i8, qd=7) == 3
-    assert call(i8, hq=64) == 4
+    assert call(i8, hq=128) == 4
     assert call(i8, scale=-1.0) == 2
     assert call(i8, n=0) == 0 and call(i8, tq=0) == 0
     assert lib.pa_prefill_varlen(dummy, 16 * 128, 16, dummy, dummy, ctypes.byref(i8), dummy, dummy, dummy, dummy,

@@ -297,6 +297,7 @@ def _int8_case_pools(case):
     (128, 16, 8, 256, [1, 2, 100, 255, 256, 257, 1000, 2048]),
     (64, 8, 8, 32, [3, 64, 129, 700]),
     (256, 8, 2, 16, [40, 300, 17, 0]),
+    (128, 32, 4, 16, [1, 500, 1500, 0, 64]),           # group 8
 ])
 def test_int8_decode_fp16_queries(d, hq, hkv, bs, ctx):
     case = W.make_decode("i8_f16", 870 + d + bs, ctx, hq, hkv, d, bs, F16)

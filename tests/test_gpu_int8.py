@@ -140,6 +140,8 @@ DECODE_SHAPES = [  # (dtype, d, hq, hkv, bs, context lengths)
     ("bf16", 64, 8, 8, 32, [3, 64, 129, 700]),                  # group 1
     ("bf16", 256, 8, 2, 16, [40, 300, 17]),                     # group 4, head_dim 256
     ("f32", 128, 8, 4, 64, [0, 5, 333]),                        # a padding row (context 0)
+    ("bf16", 128, 16, 2, 16, [1, 300, 2048, 0, 77]),            # group 8: two virtual heads per pool head
+    ("f32", 64, 32, 4, 32, [3, 64, 129, 700]),                  # group 8, head_dim 64
 ]
 
 
@@ -266,6 +268,8 @@ PREFILL_CASES = {
                                                 8, "bf16"),
     "ragged_g1_d256_f32": lambda: W.make_prefill("i8_ragged2", 902, [33, 4, 90], [7, 0, 100], 4, 4, 256, 16,
                                                  "f32"),
+    "ragged_g8_d128": lambda: W.make_prefill("i8_ragged3", 903, [50, 1, 130], [0, 20, 300], 16, 2, 128, 16,
+                                             "bf16"),
 }
 
 
