@@ -174,8 +174,8 @@ pa_status pa_decode_int8(const void *q, int64_t q_row_stride, int32_t num_q_head
  * pa_prefill_varlen, plus q_dtype (PA_BF16 / PA_F16 / PA_F32, also out's
  * type) and the fp16 scale pools; INT8 pools as for pa_decode_int8 (query
  * groups 1, 2, 4, 8).  bf16 or fp16 queries with head_dim 64 or 128, an even
- * number of KV heads, a group of 1, 2 or 4, a 16-byte aligned out and 4-byte
- * aligned scale pools run on the matrix cores (each key step's codes are dequantized to the query
+ * number of KV heads, a 16-byte aligned out and 4-byte aligned scale pools
+ * run on the matrix cores (each key step's codes are dequantized to the query
  * type in LDS; for fp16 they saturate at +-65504); every other call takes
  * each packed query token as one row of the INT8 decode pass over its
  * visible keys (vector ALU).

@@ -77,7 +77,7 @@ hipError_t launch_decode_int8(const void *q, int64_t q_row_stride, int hq, int q
 
 // Query-tiled MFMA prefill over INT8 pools with bf16 or fp16 queries
 // (q_dtype 1 or 3): each step's codes are dequantized to the query type in
-// LDS (d 64/128, even hkv, groups 1/2/4).
+// LDS (d 64/128, even hkv, groups 1/2/4/8).
 bool prefill_mfma_int8_supported(const PoolGeom &g, int group);
 hipError_t launch_prefill_mfma_int8(const void *q, int64_t q_row_stride, int hq, int q_dtype, const void *k_pool,
                                     const void *v_pool, const void *k_scale, const void *v_scale, const PoolGeom &g,

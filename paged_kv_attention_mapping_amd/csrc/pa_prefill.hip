@@ -928,7 +928,8 @@ bool prefill_mfma_int8_supported(const PoolGeom &g, int group) {
     // INT8 pools with bf16 or fp16 queries: the scale words are 4-byte pairs of heads
     // (even hkv); 16 pool rows span < 2^31 bytes
     return g.dtype == 2 && (g.d == 64 || g.d == 128) && g.block_size >= 4 && g.hkv % 2 == 0 &&
-           (group == 1 || group == 2 || group == 4) && (int64_t)g.hkv * g.d * kRowsPerWave < ((int64_t)1 << 31);
+           (group == 1 || group == 2 || group == 4 || group == 8) &&
+           (int64_t)g.hkv * g.d * kRowsPerWave < ((int64_t)1 << 31);
 }
 
 hipError_t launch_prefill_mfma_int8(const void *q, int64_t q_row_stride, int hq, int q_dtype, const void *k_pool,

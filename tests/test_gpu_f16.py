@@ -323,6 +323,7 @@ INT8_F16_PREFILL = {  # name: (q_lens, q_offsets, hq, hkv, d, bs); even hkv and 
     "group4_16_4_d128_bs32": ([128, 77], [0, 300], 16, 4, 128, 32),
     "odd_hkv_rows_path_6_3_d128": ([40, 9], [5, 0], 6, 3, 128, 16),
     "d256_rows_path": ([20, 3], [0, 11], 4, 2, 256, 16),
+    "group8_16_2_d128_bs16": ([90, 1, 200], [0, 33, 150], 16, 2, 128, 16),
 }
 
 
