@@ -849,13 +849,7 @@ RowAttnPlan plan_row_attention(int num_rows, const PoolGeom &g, int group, int m
     // while the other starts up or reduces.
     // INT8 pools: 4 waves (the int8 kernel's per-lane state needs about 150
     // registers; at 8 waves the compiler caps it at 128 and spills).
-    int waves = (group <= 2 && g.dtype != 2) ? 8 : 4;
-#ifdef PA_WAVES_OVERRIDE
-    waves = PA_WAVES_OVERRIDE;
-#endif
-#ifdef PA_I8_WAVES
-    if (g.dtype == 2) waves = group <= 2 ? PA_I8_WAVES : 4;
-#endif
+    const int waves = (group <= 2 && g.dtype != 2) ? 8 : 4;
     const int tpr = tokens_per_round(g.dtype, g.d, waves);
     // A split's keys may start anywhere in a block, so it spans at most
     // ceil(keys / block_size) + 1 blocks: keep that within the kBlkIds block
