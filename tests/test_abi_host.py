@@ -227,3 +227,27 @@ def test_validators_reject_bad_metadata():
     with pytest.raises(pa.PaError, match="row_order"):
         pa.validate_decode_metadata(dec.context_lens, dec.block_table, dec.max_context_len, pool,
                                     row_order=order)
+
+
+def test_split_plan_follows_the_documented_rule():
+    """The decode workspace reveals the planned split slots per row: enough
+    (row, KV head, split) workgroups for two rounds of resident workgroups
+    (1024 at 8 waves), at least 16 rounds of keys (1024 at bf16, head_dim
+    128) per split at max_context_len, none longer than the staged block ids
+    allow.  Pure host arithmetic: nothing is launched."""
+    lib = pa.load()
+
+    def ws(rows, hq, max_ctx, **pool):
+        p = _pool(**pool)
+        return lib.pa_decode_workspace_bytes(rows, hq, max_ctx, ctypes.byref(p))
+
+    per_split = 16 * (128 + 2) * 4                     # one row's partials for 16 query heads
+    bf = dict(nb=64, bs=16, hkv=8, d=128, dtype=pa.PA_BF16)
+    assert ws(256, 16, 2048, **bf) == 0                # 2048 units already fill the GPU: no split
+    assert ws(64, 16, 32768, **bf) == 64 * 2 * per_split      # 512 units -> 2 splits
+    assert ws(1, 16, 20000, **bf) == 1 * 20 * per_split       # min(128, ceil(20000 / 1024)) = 20
+    assert ws(8, 16, 512, **bf) == 0                   # 512 keys < 16 rounds: one split
+    assert ws(32, 16, 4096, **bf) == 32 * 4 * per_split       # min(4, 4) = 4
+    # block size 1: a split may span at most 4095 block ids (4032 keys in whole rounds)
+    one = dict(nb=1 << 20, bs=1, hkv=8, d=128, dtype=pa.PA_BF16)
+    assert ws(256, 16, 1 << 20, **one) == 256 * (-(-(1 << 20) // 4032)) * per_split
