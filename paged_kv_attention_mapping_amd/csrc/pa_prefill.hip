@@ -67,11 +67,9 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kPfWaves = 8;                   // two waves per SIMD
-constexpr int kPfThreads = 64 * kPfWaves;
 constexpr int kBN = 64;                       // keys per wave tile
-constexpr int kStep = 2 * kBN;                // keys per workgroup step: one tile per key half
-constexpr int kRowsPerWave = kStep / kPfWaves;  // step rows each wave loads (16)
+constexpr int kRowsPerWave = 16;              // step rows each wave loads (both layouts)
+constexpr int kNumCUs = 256;                  // MI355X compute units
 constexpr int kBlkWin = 1024;                 // block ids staged in LDS at a time
 constexpr float kLog2eF = 1.4426950408889634f;
 
@@ -108,9 +106,19 @@ template <> struct Mm<f16_t> {
     }
 };
 
-template <int D, int NH, typename E = bf16_t>
+// Workgroup layouts.  NW = 8: two waves per SIMD, one workgroup per CU; each
+// slot's two waves split every 128-key step into key halves and merge their
+// partial results at the end of a tile.  NW = 4: one wave per SIMD, 64-key
+// steps, no merge, and half the LDS, so two workgroups share a CU and their
+// phases (prologues, barriers, epilogues) overlap each other's matrix work.
+template <int D, int NH, typename E = bf16_t, int NW = 8>
 struct Pf {
     using M = Mm<E>;
+    static constexpr int WAVES = NW;
+    static constexpr int THREADS = 64 * NW;
+    static constexpr int KH = NW == 8 ? 2 : 1;         // key halves per step
+    static constexpr int STEP = KH * kBN;              // keys per workgroup step
+    static_assert((NW == 8 || NW == 4) && STEP / NW == kRowsPerWave, "layout");
     typedef typename M::x8 x8;
     typedef typename M::x4 x4;
     typedef typename M::x2 x2;
@@ -121,7 +129,7 @@ struct Pf {
     static constexpr int CPR = D / 8;                  // 16-byte chunks per row
     static constexpr int ROWB = D * 2;                 // bytes per LDS row (bf16)
     static constexpr int TILEB = kBN * ROWB;           // bytes of one wave tile (K or V)
-    static constexpr int STEPB = kStep * ROWB;         // bytes of one step (K or V)
+    static constexpr int STEPB = STEP * ROWB;          // bytes of one step (K or V)
     static constexpr int RPI = 64 / CPR;               // rows per wave-wide 16-byte load
     static constexpr int LPW = kRowsPerWave / RPI;     // 16-byte loads per lane per step (K or V)
     static constexpr int MERGE = DT * 16 + 2;          // floats per lane handed between key halves
@@ -129,17 +137,18 @@ struct Pf {
     // and the rows' scale words
     static constexpr int DIM = D;
     static constexpr int CPR8 = D / 16;                // 16-byte chunks per int8 row
-    static constexpr int STAGEB = kStep * D;           // bytes of one int8 step (K or V)
+    static constexpr int STAGEB = STEP * D;            // bytes of one int8 step (K or V)
     static constexpr int RPI8 = 64 / CPR8;             // int8 rows per wave-wide 16-byte load
     static constexpr int LPW8 = kRowsPerWave / RPI8;   // such loads per lane per step (K or V)
-    static constexpr int CONV = kStep * CPR8 / kPfThreads;  // int8 chunks each thread converts (K or V)
-    static constexpr int SCLB = kStep * 4;             // bytes of one step's scale words (K or V)
-    static_assert(LPW8 * RPI8 == kRowsPerWave && CONV * kPfThreads == kStep * CPR8, "int8 row split");
-    static_assert(kStep == 128 && kPfWaves >= 4, "scale words: waves 0..3 fetch 64 rows each");
-    static_assert(4 * MERGE * 64 * 4 <= 2 * STEPB + 2 * STAGEB, "merge area fits in the INT8 layout");
+    static constexpr int CONV = STEP * CPR8 / THREADS;  // int8 chunks each thread converts (K or V)
+    static constexpr int SCLB = STEP * 4;              // bytes of one step's scale words (K or V)
+    // the INT8 staging (8-wave layout only): waves 0..3 fetch 64 scale words each
+    static_assert(NW != 8 || (LPW8 * RPI8 == kRowsPerWave && CONV * THREADS == STEP * CPR8 && STEP == 128),
+                  "int8 row split");
+    static_assert(NW != 8 || 4 * MERGE * 64 * 4 <= 2 * STEPB + 2 * STAGEB, "merge area fits in the INT8 layout");
     static_assert(LPW * RPI == kRowsPerWave && LPW >= 1, "row split");
     static_assert((4 * RPI) % CPR == 0, "V swizzle independent of the load index");
-    static_assert(4 * MERGE * 64 * 4 <= 4 * STEPB, "merge area fits in the K/V buffers");
+    static_assert(NW != 8 || 4 * MERGE * 64 * 4 <= 4 * STEPB, "merge area fits in the K/V buffers");
 };
 
 struct PfArgs {
@@ -260,7 +269,7 @@ __device__ __forceinline__ void load_wave_rows(const PfArgs &a, int kb_step, int
                                                int win0, int blk0, int64_t kv_row, int64_t kv_head,
                                                const uint32_t (&koff)[C::LPW], uint32_t voff, int w, int lane,
                                                const int *s_blk, unsigned char *dk, unsigned char *dv) {
-    if (kb_step + kBN * (w / (kPfWaves / 2)) > kmax) return;
+    if (kb_step + kBN * (C::KH == 2 ? w / (C::WAVES / 2) : 0) > kmax) return;
     const int row0 = __builtin_amdgcn_readfirstlane(kb_step + kRowsPerWave * w);
     if (shift >= 4 && row0 + kRowsPerWave - 1 <= kmax) {
         const int p = __builtin_amdgcn_readfirstlane(s_blk[(row0 >> shift) - win0]);
@@ -325,7 +334,7 @@ __device__ __forceinline__ void load_wave_rows_i8(const PfArgs &a, int kb_step, 
         global_lds4(sp + slot_of(kb_step + r) * a.hkv + (g & ~1),
                     __builtin_amdgcn_readfirstlane(lds_addr(w < 2 ? dsk : dsv) + (w & 1) * 256));
     }
-    if (kb_step + kBN * (w / (kPfWaves / 2)) > kmax) return;
+    if (kb_step + kBN * (C::KH == 2 ? w / (C::WAVES / 2) : 0) > kmax) return;
     const int row0 = __builtin_amdgcn_readfirstlane(kb_step + kRowsPerWave * w);
     if (shift >= 4 && row0 + kRowsPerWave - 1 <= kmax) {
         const int p = __builtin_amdgcn_readfirstlane(s_blk[(row0 >> shift) - win0]);
@@ -369,7 +378,7 @@ __device__ __forceinline__ void convert_step_i8(const unsigned char *k8, const u
     constexpr bool kF16 = std::is_same<typename C::x8, Mm<f16_t>::x8>::value;
 #pragma unroll
     for (int t = 0; t < C::CONV; ++t) {
-        const int cid = tid + kPfThreads * t;
+        const int cid = tid + C::THREADS * t;
         const int r = cid / C::CPR8, c8 = cid % C::CPR8;
 #pragma unroll
         for (int kv = 0; kv < 2; ++kv) {
@@ -617,9 +626,12 @@ __device__ __forceinline__ void load_and_attend(const PfArgs &a, bool load, int 
     if (tile) attend_tile<C>(cur, cur, kofs, vofs, qf, st, need_mask, thr, c);
 }
 
-template <int D, int NH, bool I8, typename E>
-__global__ __launch_bounds__(kPfThreads, 1) void prefill_mfma_kernel(PfArgs a) {
-    using C = Pf<D, NH, E>;
+template <int D, int NH, bool I8, typename E, int NW>
+__global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void prefill_mfma_kernel(PfArgs a) {
+    static_assert(!I8 || NW == 8, "INT8 pools use the 8-wave layout");
+    using C = Pf<D, NH, E, NW>;
+    constexpr int kStep = C::STEP;
+    constexpr int kPfThreads = C::THREADS;
     // [K, V][buffer][step rows] bf16 step buffers: every buffer and block
     // offset of an LDS read is an immediate.  bf16 pools: two buffers, the
     // next step loading while this one is computed.  INT8 pools: one bf16
@@ -641,8 +653,8 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_mfma_kernel(PfArgs a) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = tid >> 6;
     const int n = lane & 31, hf = lane >> 5;
-    const int kh = w / (kPfWaves / 2);  // key half: tile kh of every step
-    const int wl = w % (kPfWaves / 2);  // (head, position sub-tile) slot
+    const int kh = C::KH == 2 ? w / (C::WAVES / 2) : 0;  // key half: tile kh of every step
+    const int wl = w % (C::WAVES / C::KH);               // (head, position sub-tile) slot
 
     int64_t wg = blockIdx.x;
     const int g = (int)(wg % a.hkv);
@@ -820,25 +832,45 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_mfma_kernel(PfArgs a) {
             }
         }
 
-        // ---- the second key half hands (O, m, l) to the first through LDS
-        if (kh == 1) {
-#pragma unroll
-            for (int dt = 0; dt < C::DT; ++dt)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) merge[(dt * 16 + r) * 64 + lane] = sm.o[dt][r];
-            merge[(C::DT * 16) * 64 + lane] = sm.m;
-            merge[(C::DT * 16 + 1) * 64 + lane] = sm.l;
-        }
-        __syncthreads();
-        if (kh == 0) {
-            const float m2 = merge[(C::DT * 16) * 64 + lane];
-            const float l2 = merge[(C::DT * 16 + 1) * 64 + lane];
-            const float mn = fmaxf(sm.m, m2);
-            const float a1 = (sm.m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((sm.m - mn) * c);
-            const float a2 = (m2 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m2 - mn) * c);
-            const float l = sm.l * a1 + l2 * a2;
-            // ---- epilogue: O = O^T / l; lane (n, hf) holds d = 32dt + 8b + 4hf + a at register a + 4b
-            const float l_tot = halves_sum(l);
+        if constexpr (C::KH == 2) {
+            // ---- the second key half hands (O, m, l) to the first through LDS
+            if (kh == 1) {
+    #pragma unroll
+                for (int dt = 0; dt < C::DT; ++dt)
+    #pragma unroll
+                    for (int r = 0; r < 16; ++r) merge[(dt * 16 + r) * 64 + lane] = sm.o[dt][r];
+                merge[(C::DT * 16) * 64 + lane] = sm.m;
+                merge[(C::DT * 16 + 1) * 64 + lane] = sm.l;
+            }
+            __syncthreads();
+            if (kh == 0) {
+                const float m2 = merge[(C::DT * 16) * 64 + lane];
+                const float l2 = merge[(C::DT * 16 + 1) * 64 + lane];
+                const float mn = fmaxf(sm.m, m2);
+                const float a1 = (sm.m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((sm.m - mn) * c);
+                const float a2 = (m2 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m2 - mn) * c);
+                const float l = sm.l * a1 + l2 * a2;
+                // ---- epilogue: O = O^T / l; lane (n, hf) holds d = 32dt + 8b + 4hf + a at register a + 4b
+                const float l_tot = halves_sum(l);
+                const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+                if (row_ok) {
+    #pragma unroll
+                    for (int dt = 0; dt < C::DT; ++dt)
+    #pragma unroll
+                        for (int b = 0; b < 4; ++b) {
+                            f32x4 v;
+    #pragma unroll
+                            for (int a4 = 0; a4 < 4; ++a4) {
+                                const int r = 4 * b + a4;
+                                v[a4] = (sm.o[dt][r] * a1 + merge[(dt * 16 + r) * 64 + lane] * a2) * inv;
+                            }
+                            *reinterpret_cast<typename C::x4 *>(orow + 32 * dt + 8 * b + 4 * hf) =
+                                __builtin_convertvector(v, typename C::x4);
+                        }
+                }
+            }
+        } else {  // one wave per slot: O^T / l straight out
+            const float l_tot = halves_sum(sm.l);
             const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
             if (row_ok) {
 #pragma unroll
@@ -847,10 +879,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_mfma_kernel(PfArgs a) {
                     for (int b = 0; b < 4; ++b) {
                         f32x4 v;
 #pragma unroll
-                        for (int a4 = 0; a4 < 4; ++a4) {
-                            const int r = 4 * b + a4;
-                            v[a4] = (sm.o[dt][r] * a1 + merge[(dt * 16 + r) * 64 + lane] * a2) * inv;
-                        }
+                        for (int a4 = 0; a4 < 4; ++a4) v[a4] = sm.o[dt][4 * b + a4] * inv;
                         *reinterpret_cast<typename C::x4 *>(orow + 32 * dt + 8 * b + 4 * hf) =
                             __builtin_convertvector(v, typename C::x4);
                     }
@@ -860,26 +889,26 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_mfma_kernel(PfArgs a) {
     }
 }
 
-template <int D, int NH, bool I8, typename E>
+template <int D, int NH, bool I8, typename E, int NW>
 hipError_t run(const PfArgs &a, int num_seqs, int max_seqlen_q, hipStream_t stream) {
-    using C = Pf<D, NH, E>;
+    using C = Pf<D, NH, E, NW>;
     PfArgs b = a;
     const int max_tiles = (max_seqlen_q + C::BM - 1) / C::BM;
     b.pairs_per_seq = (max_tiles + 1) / 2;
     b.head_groups = a.group / NH;
     const int64_t wgs = (int64_t)num_seqs * b.pairs_per_seq * b.head_groups * a.hkv;
     if (wgs == 0) return hipSuccess;
-    hipLaunchKernelGGL((prefill_mfma_kernel<D, NH, I8, E>), dim3((unsigned)wgs), dim3(kPfThreads), 0, stream, b);
+    hipLaunchKernelGGL((prefill_mfma_kernel<D, NH, I8, E, NW>), dim3((unsigned)wgs), dim3(C::THREADS), 0, stream, b);
     return hipGetLastError();
 }
 
-template <int D, bool I8 = false, typename E = bf16_t>
+template <int D, bool I8 = false, typename E = bf16_t, int NW = 8>
 hipError_t dispatch_nh(const PfArgs &a, int num_seqs, int max_seqlen_q, hipStream_t stream) {
     switch (a.group) {
-        case 1: return run<D, 1, I8, E>(a, num_seqs, max_seqlen_q, stream);
-        case 2: return run<D, 2, I8, E>(a, num_seqs, max_seqlen_q, stream);
-        case 4: return run<D, 4, I8, E>(a, num_seqs, max_seqlen_q, stream);
-        case 8: return run<D, 4, I8, E>(a, num_seqs, max_seqlen_q, stream);
+        case 1: return run<D, 1, I8, E, NW>(a, num_seqs, max_seqlen_q, stream);
+        case 2: return run<D, 2, I8, E, NW>(a, num_seqs, max_seqlen_q, stream);
+        case 4: return run<D, 4, I8, E, NW>(a, num_seqs, max_seqlen_q, stream);
+        case 8: return run<D, 4, I8, E, NW>(a, num_seqs, max_seqlen_q, stream);
     }
     return hipErrorInvalidValue;
 }
@@ -917,11 +946,25 @@ hipError_t launch_prefill_mfma(const void *q, int64_t q_row_stride, int hq, cons
     a.scale_log2 = softmax_scale * kLog2eF;
     a.out = reinterpret_cast<uint16_t *>(out);
     if (max_seqlen_q <= 0) return hipSuccess;
+    // Layout: the 8-wave workgroup while the launch fits the CUs in one round
+    // (a long prompt: every workgroup streams many steps); the 4-wave one,
+    // two per CU, once there are more workgroups than CUs (many or short
+    // sequences), so one workgroup's prologue and epilogue overlap another's
+    // matrix work.  The grid has the same size in both layouts.
+    const int nh = a.group >= 4 ? 4 : a.group;
+    const int bm = 32 * (4 / nh);
+    const int64_t pairs = (((int64_t)max_seqlen_q + bm - 1) / bm + 1) / 2;
+    const int64_t grid = (int64_t)num_seqs * pairs * (a.group / nh) * a.hkv;
+    const bool w4 = grid > kNumCUs;
     if (g.dtype == 3)
-        return g.d == 128 ? dispatch_nh<128, false, f16_t>(a, num_seqs, max_seqlen_q, stream)
-                          : dispatch_nh<64, false, f16_t>(a, num_seqs, max_seqlen_q, stream);
-    return g.d == 128 ? dispatch_nh<128>(a, num_seqs, max_seqlen_q, stream)
-                      : dispatch_nh<64>(a, num_seqs, max_seqlen_q, stream);
+        return g.d == 128 ? (w4 ? dispatch_nh<128, false, f16_t, 4>(a, num_seqs, max_seqlen_q, stream)
+                                : dispatch_nh<128, false, f16_t, 8>(a, num_seqs, max_seqlen_q, stream))
+                          : (w4 ? dispatch_nh<64, false, f16_t, 4>(a, num_seqs, max_seqlen_q, stream)
+                                : dispatch_nh<64, false, f16_t, 8>(a, num_seqs, max_seqlen_q, stream));
+    return g.d == 128 ? (w4 ? dispatch_nh<128, false, bf16_t, 4>(a, num_seqs, max_seqlen_q, stream)
+                            : dispatch_nh<128, false, bf16_t, 8>(a, num_seqs, max_seqlen_q, stream))
+                      : (w4 ? dispatch_nh<64, false, bf16_t, 4>(a, num_seqs, max_seqlen_q, stream)
+                            : dispatch_nh<64, false, bf16_t, 8>(a, num_seqs, max_seqlen_q, stream));
 }
 
 bool prefill_mfma_int8_supported(const PoolGeom &g, int group) {

@@ -219,3 +219,25 @@ def test_mixed_decode_rows_and_chunks_in_one_launch(dtype):
     err = max_abs_err(got, ref)
     say(f"  max-abs {err:.3e}")
     assert err <= tol(dtype)
+
+
+@pytest.mark.parametrize("dtype,d,hq,hkv,bs", [
+    ("bf16", 128, 16, 8, 16), ("bf16", 64, 8, 1, 32), ("bf16", 128, 4, 4, 16), ("bf16", 64, 16, 4, 8),
+    ("f16", 128, 16, 8, 256), ("f16", 64, 8, 2, 16), ("bf16", 128, 32, 4, 16),
+])
+def test_many_short_sequences_two_workgroups_per_cu(dtype, d, hq, hkv, bs):
+    """80 sequences of 1..200 new tokens after 0..300 cached ones: the launch
+    has more workgroups than CUs, which selects the 4-wave layout (two
+    workgroups per CU, 64-key steps, no key-half merge)."""
+    rng = np.random.default_rng(7600 + d + hq + hkv)
+    q_lens = rng.integers(1, 200, size=80, endpoint=True).tolist()
+    q_offs = rng.integers(0, 300, size=80, endpoint=True).tolist()
+    case = W.make_prefill("many", 7600 + d + hq, q_lens, q_offs, hq, hkv, d, bs, dtype)
+    nh = min(hq // hkv, 4)
+    pairs = (-(-case.max_seqlen_q // (32 * (4 // nh))) + 1) // 2
+    assert 80 * pairs * (hq // hkv // nh) * hkv > 256, "the case must exceed one workgroup per CU"
+    say(f"[prefill] 80 short sequences {dtype} d={d} {hq}/{hkv} bs={bs}")
+    got, ref, _ = run_prefill(case)
+    err = max_abs_err(got, ref)
+    say(f"  max-abs {err:.3e}")
+    assert err <= tol(dtype)
