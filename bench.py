@@ -400,7 +400,8 @@ def mixed_prefill_measure(pa, W, reps):
             "workload": f"chunked prefill batch: {mx.num_seqs} sequences, {mx.total_q} new tokens, block 16, bf16",
             "avg_launch_us": round(ms * 1e3, 2), "flops_per_launch": flops,
             "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
-                         "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)}}
+                         "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                         "traffic": measured_traffic("prefill_mixed")}}
 
 
 def graph_measure(step, eager_ms_per_step, reps):
