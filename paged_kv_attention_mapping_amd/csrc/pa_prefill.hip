@@ -142,8 +142,8 @@ struct Pf {
     static constexpr int LPW8 = kRowsPerWave / RPI8;   // such loads per lane per step (K or V)
     static constexpr int CONV = STEP * CPR8 / THREADS;  // int8 chunks each thread converts (K or V)
     static constexpr int SCLB = STEP * 4;              // bytes of one step's scale words (K or V)
-    // the INT8 staging (8-wave layout only): waves 0..3 fetch 64 scale words each
-    static_assert(NW != 8 || (LPW8 * RPI8 == kRowsPerWave && CONV * THREADS == STEP * CPR8 && STEP == 128),
+    // the INT8 staging: 2 * STEP / 64 waves fetch 64 scale words each
+    static_assert(LPW8 * RPI8 == kRowsPerWave && CONV * THREADS == STEP * CPR8 && 2 * STEP / 64 <= NW,
                   "int8 row split");
     static_assert(NW != 8 || 4 * MERGE * 64 * 4 <= 2 * STEPB + 2 * STAGEB, "merge area fits in the INT8 layout");
     static_assert(LPW * RPI == kRowsPerWave && LPW >= 1, "row split");
@@ -328,11 +328,12 @@ __device__ __forceinline__ void load_wave_rows_i8(const PfArgs &a, int kb_step, 
         const int p = key <= kmax ? s_blk[(key >> shift) - win0] : -1;
         return p >= 0 ? ((int64_t)p << shift) + (key & bmask) : (blk0 >= 0 ? ((int64_t)blk0 << shift) : 0);
     };
-    if (w < 4) {
-        const int r = (w & 1) * 64 + lane;
-        const uint16_t *sp = w < 2 ? a.k_scale : a.v_scale;
+    constexpr int SW = C::STEP / 64;  // waves fetching each of K's and V's scale words, 64 rows each
+    if (w < 2 * SW) {
+        const int r = (w % SW) * 64 + lane;
+        const uint16_t *sp = w < SW ? a.k_scale : a.v_scale;
         global_lds4(sp + slot_of(kb_step + r) * a.hkv + (g & ~1),
-                    __builtin_amdgcn_readfirstlane(lds_addr(w < 2 ? dsk : dsv) + (w & 1) * 256));
+                    __builtin_amdgcn_readfirstlane(lds_addr(w < SW ? dsk : dsv) + (w % SW) * 256));
     }
     if (kb_step + kBN * (C::KH == 2 ? w / (C::WAVES / 2) : 0) > kmax) return;
     const int row0 = __builtin_amdgcn_readfirstlane(kb_step + kRowsPerWave * w);
@@ -628,7 +629,6 @@ __device__ __forceinline__ void load_and_attend(const PfArgs &a, bool load, int 
 
 template <int D, int NH, bool I8, typename E, int NW>
 __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void prefill_mfma_kernel(PfArgs a) {
-    static_assert(!I8 || NW == 8, "INT8 pools use the 8-wave layout");
     using C = Pf<D, NH, E, NW>;
     constexpr int kStep = C::STEP;
     constexpr int kPfThreads = C::THREADS;
@@ -913,6 +913,15 @@ hipError_t dispatch_nh(const PfArgs &a, int num_seqs, int max_seqlen_q, hipStrea
     return hipErrorInvalidValue;
 }
 
+// Workgroups of a launch (the same in both layouts): sequences x tile pairs
+// at max_seqlen_q x head groups x KV heads.
+int64_t prefill_grid(int group, int hkv, int num_seqs, int max_seqlen_q) {
+    const int nh = group >= 4 ? 4 : group;
+    const int bm = 32 * (4 / nh);
+    const int64_t pairs = (((int64_t)max_seqlen_q + bm - 1) / bm + 1) / 2;
+    return (int64_t)num_seqs * pairs * (group / nh) * hkv;
+}
+
 }  // namespace
 
 bool prefill_mfma_supported(const PoolGeom &g, int group) {
@@ -951,11 +960,7 @@ hipError_t launch_prefill_mfma(const void *q, int64_t q_row_stride, int hq, cons
     // two per CU, once there are more workgroups than CUs (many or short
     // sequences), so one workgroup's prologue and epilogue overlap another's
     // matrix work.  The grid has the same size in both layouts.
-    const int nh = a.group >= 4 ? 4 : a.group;
-    const int bm = 32 * (4 / nh);
-    const int64_t pairs = (((int64_t)max_seqlen_q + bm - 1) / bm + 1) / 2;
-    const int64_t grid = (int64_t)num_seqs * pairs * (a.group / nh) * a.hkv;
-    const bool w4 = grid > kNumCUs;
+    const bool w4 = prefill_grid(a.group, a.hkv, num_seqs, max_seqlen_q) > kNumCUs;
     if (g.dtype == 3)
         return g.d == 128 ? (w4 ? dispatch_nh<128, false, f16_t, 4>(a, num_seqs, max_seqlen_q, stream)
                                 : dispatch_nh<128, false, f16_t, 8>(a, num_seqs, max_seqlen_q, stream))
@@ -1001,11 +1006,16 @@ hipError_t launch_prefill_mfma_int8(const void *q, int64_t q_row_stride, int hq,
     a.scale_log2 = softmax_scale * kLog2eF;
     a.out = reinterpret_cast<uint16_t *>(out);
     if (max_seqlen_q <= 0) return hipSuccess;
+    const bool w4 = prefill_grid(a.group, a.hkv, num_seqs, max_seqlen_q) > kNumCUs;  // as for 16-bit pools
     if (q_dtype == 3)  // fp16 queries: the codes dequantize to fp16, fp16 MFMA
-        return g.d == 128 ? dispatch_nh<128, true, f16_t>(a, num_seqs, max_seqlen_q, stream)
-                          : dispatch_nh<64, true, f16_t>(a, num_seqs, max_seqlen_q, stream);
-    return g.d == 128 ? dispatch_nh<128, true>(a, num_seqs, max_seqlen_q, stream)
-                      : dispatch_nh<64, true>(a, num_seqs, max_seqlen_q, stream);
+        return g.d == 128 ? (w4 ? dispatch_nh<128, true, f16_t, 4>(a, num_seqs, max_seqlen_q, stream)
+                                : dispatch_nh<128, true, f16_t, 8>(a, num_seqs, max_seqlen_q, stream))
+                          : (w4 ? dispatch_nh<64, true, f16_t, 4>(a, num_seqs, max_seqlen_q, stream)
+                                : dispatch_nh<64, true, f16_t, 8>(a, num_seqs, max_seqlen_q, stream));
+    return g.d == 128 ? (w4 ? dispatch_nh<128, true, bf16_t, 4>(a, num_seqs, max_seqlen_q, stream)
+                            : dispatch_nh<128, true, bf16_t, 8>(a, num_seqs, max_seqlen_q, stream))
+                      : (w4 ? dispatch_nh<64, true, bf16_t, 4>(a, num_seqs, max_seqlen_q, stream)
+                            : dispatch_nh<64, true, bf16_t, 8>(a, num_seqs, max_seqlen_q, stream));
 }
 
 }  // namespace pa

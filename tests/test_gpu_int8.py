@@ -372,3 +372,32 @@ def test_prefill_int8_c5a_4096_sampled_rows():
     err = max_abs_err(out[torch.as_tensor(rows, device="cuda").long()], ref)
     say(f"  max-abs {err:.3e}")
     assert err <= tol("bf16")
+
+
+@pytest.mark.parametrize("qdtype,d,hq,hkv", [("bf16", 128, 16, 8), ("f16", 128, 16, 8), ("bf16", 64, 8, 2),
+                                             ("f16", 128, 32, 4)])
+def test_prefill_int8_many_short_sequences(qdtype, d, hq, hkv):
+    """80 sequences of 1..200 new tokens after 0..300 cached ones over INT8
+    pools: more workgroups than CUs, which selects the 4-wave layout (64-key
+    steps, two scale-fetching waves)."""
+    rng = np.random.default_rng(9500 + d + hq)
+    q_lens = rng.integers(1, 200, size=80, endpoint=True).tolist()
+    q_offs = rng.integers(0, 300, size=80, endpoint=True).tolist()
+    case = W.make_prefill("i8_many", 9500 + d + hq, q_lens, q_offs, hq, hkv, d, 16, qdtype)
+    say(f"[int8 prefill] 80 short sequences, {qdtype} queries, d={d} {hq}/{hkv}")
+    nb, bs, _, _ = case.empty_pools()[0].shape
+    host = int8_pools(nb, bs, hkv, d)
+    dev = dev_pools(*host)
+    for k, v, sl in ((case.k_cached, case.v_cached, case.slot_cached), (case.k_new, case.v_new, case.slot_new)):
+        if len(sl):
+            pa.pa_store_kv_int8(to_dev(k), to_dev(v), to_dev(sl), *dev)
+            Q.store_kv(k, v, sl, *host)
+    offs = np.asarray(case.q_offsets, np.int32)
+    out = pa.pa_prefill_varlen_int8(to_dev(case.q), *dev, to_dev(case.cu_seqlens_q), to_dev(case.cu_seqlens_k),
+                                    to_dev(offs), to_dev(case.block_table), case.max_seqlen_q, case.max_seqlen_k,
+                                    case.scale)
+    torch.cuda.synchronize()
+    ref = Q.prefill(case.q, *host, case.cu_seqlens_q, case.cu_seqlens_k, offs, case.block_table, case.scale)
+    err = max_abs_err(out, ref)
+    say(f"  max-abs {err:.3e}")
+    assert err <= tol(qdtype)
