@@ -18,10 +18,15 @@
 //  * a wave owns 32 query positions of ONE query head; four (head, position
 //    sub-tile) slots cover NH query heads that share one KV head (GQA) times
 //    4/NH sub-tiles, so one K/V tile in LDS serves all of them.
-//  * a workgroup has eight waves, two per SIMD: each slot is held by two
-//    waves that split the keys.  A step stages 128 keys; the first key half
-//    takes keys 0..63 of it, the second keys 64..127.  At the end the second
-//    half hands its (O, m, l) to the first through LDS, which merges them.
+//  * two workgroup layouts.  8 waves, two per SIMD, one workgroup per CU:
+//    each slot is held by two waves that split the keys.  A step stages 128
+//    keys; the first key half takes keys 0..63 of it, the second keys
+//    64..127.  At the end the second half hands its (O, m, l) to the first
+//    through LDS, which merges them.  4 waves, one per SIMD: 64-key steps,
+//    one wave per slot, half the LDS, so two workgroups share a CU and one's
+//    prologue, barriers and epilogue overlap the other's matrix work.  The
+//    host takes the 8-wave layout when the launch fits the CUs in one round
+//    (long prompts) and the 4-wave one otherwise (many or short sequences).
 //  * scores are computed transposed, S^T = K . Q^T (A = K rows from LDS,
 //    B = the wave's Q held in registers all along), so each lane owns one
 //    query's column: sums need one exchange between the two lane halves.
