@@ -190,6 +190,7 @@ def main():
 
     graph = None if args.no_graph else graph_measure(step, ms_per_step, max(args.steps, 2))
     mixed = mixed_prefill_measure(pa, W, max(args.steps, 2))
+    small = small_configs_measure(pa, W)
 
     f16 = None if args.no_f16 else f16_measure(pa, W, lay, ctx_d, bt_d, order_d, dec_call_ms, pf_call_ms,
                                                max(args.steps, 2))
@@ -252,6 +253,7 @@ def main():
     if graph is not None:
         result["graph_step"] = graph
     result["prefill_mixed"] = mixed
+    result["small_configs"] = small
     print(json.dumps(result), flush=True)
 
 
@@ -402,6 +404,74 @@ def mixed_prefill_measure(pa, W, reps):
             "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
                          "traffic": measured_traffic("prefill_mixed")}}
+
+
+def _time_in_graph(fn, calls=20, replays=5):
+    """Mean duration (ms) of one call of fn, from `calls` calls captured in one
+    HIP graph and replayed: for launches shorter than the host's own launch
+    work, which per-call events would measure instead."""
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(calls):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(replays):
+        g.replay()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / (replays * calls)
+
+
+def small_configs_measure(pa, W):
+    """Per-call times of the small prefill shapes (not part of the step): the
+    tiny fp32 batch (3 prompts of 5, 17, 40 tokens, d 32, block 16, and one
+    decode step of its 3 rows), 8 prompts of 32, 128 and 256 tokens, and 2
+    suffixes of 44 tokens after 256 cached (16/8 heads, d 128, bf16, block
+    256).  These launches are latency-bound, shorter than the host's work to
+    launch them, so each is timed inside a HIP graph of 20 calls."""
+    import torch
+    dev = "cuda"
+    i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)  # noqa: E731
+    res = {}
+
+    def prefill_leg(name, case, seed):
+        shape = (case.num_blocks, case.block_size, case.num_kv_heads, case.head_dim)
+        if case.dtype == "f32":
+            kp = torch.randn(shape, generator=torch.Generator().manual_seed(seed)).to(dev)
+            vp = torch.randn(shape, generator=torch.Generator().manual_seed(seed + 1)).to(dev)
+            q = torch.from_numpy(np.ascontiguousarray(case.q)).to(dev)
+        else:
+            kp, vp = W.device_normal(shape, seed), W.device_normal(shape, seed + 1)
+            q = W.device_normal((case.total_q, case.num_q_heads, case.head_dim), seed + 2)
+        out = torch.empty_like(q)
+        args = (i32(case.cu_seqlens_q), i32(case.cu_seqlens_k), i32(case.q_offsets), i32(case.block_table))
+        ms = _time_in_graph(lambda: pa.pa_prefill_varlen(q, kp, vp, *args, case.max_seqlen_q, case.max_seqlen_k,
+                                                         case.scale, out=out))
+        flops = 4.0 * case.head_dim * case.num_q_heads * case.causal_pairs
+        res[name] = {"tokens": case.total_q, "avg_launch_us": round(ms * 1e3, 2),
+                     "tflops": round(flops / (ms * 1e-3) / 1e12, 2)}
+        return kp, vp
+
+    pre, dec = W.c1_tiny()
+    kp, vp = prefill_leg("c1_prefill_fp32", pre, 6100)
+    st = dec[0]
+    q1 = torch.from_numpy(np.ascontiguousarray(st["q"])).to(dev)
+    ctx1, bt1 = i32(st["context_lens"]), i32(pre.block_table)
+    out1 = torch.empty_like(q1)
+    ms = _time_in_graph(lambda: pa.pa_decode(q1, kp, vp, ctx1, bt1, int(st["context_lens"].max()), pre.scale,
+                                             out=out1))
+    res["c1_decode_fp32"] = {"rows": 3, "avg_launch_us": round(ms * 1e3, 2)}
+    for n in (32, 128, 256):
+        prefill_leg(f"c2_prefill_8x{n}", W.c2_varlen(n, with_values=False), 6200 + n)
+    prefill_leg("c3_prefill_2x44_after_256", W.c3_prefix(with_values=False), 6300)
+    return res
 
 
 def graph_measure(step, eager_ms_per_step, reps):

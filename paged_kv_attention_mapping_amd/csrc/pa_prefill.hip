@@ -49,7 +49,9 @@
 //    block's probabilities would grow too large (see attend_tile), so the hot
 //    path computes no per-tile max.
 //  * a workgroup processes a PAIR of query tiles of one sequence, tile p and
-//    tile T-1-p, so every workgroup of a sequence does the same causal work.
+//    tile T-1-p, so every workgroup of a sequence does the same causal work;
+//    a launch whose single tiles all fit the CUs at once takes one tile per
+//    workgroup, so its time is one tile's latency chain instead of two.
 //  * the KV head index varies fastest across workgroups; with 8 KV heads and
 //    workgroups dealt round-robin to the 8 XCDs, all tiles of one KV head run
 //    on one XCD and re-read its K/V from that XCD's L2.
@@ -171,7 +173,8 @@ struct PfArgs {
     const int32_t *cu_q;
     const int32_t *cu_k;
     const int32_t *q_off;
-    int pairs_per_seq;
+    int units_per_seq;      // work units (tile pairs, or single tiles) per sequence
+    int single;             // 1: a unit is one query tile; 0: the pair (p, T-1-p)
     int total_q;            // rows of q and out: packed rows past it are never touched
     float scale_log2;
     uint16_t *out;
@@ -666,8 +669,8 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void prefill_mfma_kernel(
     wg /= a.hkv;
     const int hgrp = (int)(wg % a.head_groups);
     wg /= a.head_groups;
-    const int pair = (int)(wg % a.pairs_per_seq);
-    const int s = (int)(wg / a.pairs_per_seq);
+    const int pair = (int)(wg % a.units_per_seq);
+    const int s = (int)(wg / a.units_per_seq);
 
     // rows outside [0, total_q) are never read or written, whatever cu_seqlens_q holds
     const int q_start = min(max(a.cu_q[s], 0), a.total_q);
@@ -675,7 +678,7 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void prefill_mfma_kernel(
     const int k_len = a.cu_k[s + 1] - a.cu_k[s];
     const int q_off = a.q_off[s];
     const int T = (q_len + C::BM - 1) / C::BM;
-    if (pair >= (T + 1) / 2) return;
+    if (pair >= (a.single ? T : (T + 1) / 2)) return;
 
     const int hh = wl % NH, sub = wl / NH;
     const int h = g * a.group + hgrp * NH + hh;
@@ -722,8 +725,8 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void prefill_mfma_kernel(
     float *merge = reinterpret_cast<float *>(s_mem) + wl * (C::MERGE * 64);
 
     for (int it = 0; it < 2; ++it) {
-        const int tile = it == 0 ? T - 1 - pair : pair;
-        if (it == 1 && tile == T - 1 - pair) break;
+        const int tile = a.single ? pair : (it == 0 ? T - 1 - pair : pair);
+        if (it == 1 && (a.single || tile == T - 1 - pair)) break;
 
         const int i_wg0 = tile * C::BM;
         const int i_wg_last = min(i_wg0 + C::BM, q_len) - 1;
@@ -899,9 +902,9 @@ hipError_t run(const PfArgs &a, int num_seqs, int max_seqlen_q, hipStream_t stre
     using C = Pf<D, NH, E, NW>;
     PfArgs b = a;
     const int max_tiles = (max_seqlen_q + C::BM - 1) / C::BM;
-    b.pairs_per_seq = (max_tiles + 1) / 2;
+    b.units_per_seq = a.single ? max_tiles : (max_tiles + 1) / 2;
     b.head_groups = a.group / NH;
-    const int64_t wgs = (int64_t)num_seqs * b.pairs_per_seq * b.head_groups * a.hkv;
+    const int64_t wgs = (int64_t)num_seqs * b.units_per_seq * b.head_groups * a.hkv;
     if (wgs == 0) return hipSuccess;
     hipLaunchKernelGGL((prefill_mfma_kernel<D, NH, I8, E, NW>), dim3((unsigned)wgs), dim3(C::THREADS), 0, stream, b);
     return hipGetLastError();
@@ -918,13 +921,29 @@ hipError_t dispatch_nh(const PfArgs &a, int num_seqs, int max_seqlen_q, hipStrea
     return hipErrorInvalidValue;
 }
 
-// Workgroups of a launch (the same in both layouts): sequences x tile pairs
-// at max_seqlen_q x head groups x KV heads.
-int64_t prefill_grid(int group, int hkv, int num_seqs, int max_seqlen_q) {
+// Workgroups of a launch (the same in both layouts): sequences x work units
+// at max_seqlen_q x head groups x KV heads, a unit being a pair of query
+// tiles, or a single tile.
+int64_t prefill_grid(int group, int hkv, int num_seqs, int max_seqlen_q, bool single) {
     const int nh = group >= 4 ? 4 : group;
     const int bm = 32 * (4 / nh);
-    const int64_t pairs = (((int64_t)max_seqlen_q + bm - 1) / bm + 1) / 2;
-    return (int64_t)num_seqs * pairs * (group / nh) * hkv;
+    const int64_t tiles = ((int64_t)max_seqlen_q + bm - 1) / bm;
+    return (int64_t)num_seqs * (single ? tiles : (tiles + 1) / 2) * (group / nh) * hkv;
+}
+
+// Work units and layout of a launch.  Pairs of query tiles (p, T-1-p) give
+// every workgroup of a sequence the same causal work, which balances launches
+// of more than one round of workgroups.  A launch whose single tiles all fit
+// the CUs at once (short prompts, small batches) takes one tile per
+// workgroup instead: its time is then one tile's latency chain (metadata,
+// block ids, first keys, epilogue), not two in a row.  Layout: the 8-wave
+// workgroup while the launch fits the CUs in one round (every workgroup
+// streams its keys alone on a CU); the 4-wave one, two per CU, once there are
+// more workgroups than CUs (many or short sequences), so one workgroup's
+// prologue and epilogue overlap another's matrix work.
+void plan_prefill(PfArgs &a, int num_seqs, int max_seqlen_q, bool &w4) {
+    a.single = prefill_grid(a.group, a.hkv, num_seqs, max_seqlen_q, true) <= kNumCUs ? 1 : 0;
+    w4 = prefill_grid(a.group, a.hkv, num_seqs, max_seqlen_q, false) > kNumCUs;
 }
 
 }  // namespace
@@ -960,12 +979,8 @@ hipError_t launch_prefill_mfma(const void *q, int64_t q_row_stride, int hq, cons
     a.scale_log2 = softmax_scale * kLog2eF;
     a.out = reinterpret_cast<uint16_t *>(out);
     if (max_seqlen_q <= 0) return hipSuccess;
-    // Layout: the 8-wave workgroup while the launch fits the CUs in one round
-    // (a long prompt: every workgroup streams many steps); the 4-wave one,
-    // two per CU, once there are more workgroups than CUs (many or short
-    // sequences), so one workgroup's prologue and epilogue overlap another's
-    // matrix work.  The grid has the same size in both layouts.
-    const bool w4 = prefill_grid(a.group, a.hkv, num_seqs, max_seqlen_q) > kNumCUs;
+    bool w4;
+    plan_prefill(a, num_seqs, max_seqlen_q, w4);
     if (g.dtype == 3)
         return g.d == 128 ? (w4 ? dispatch_nh<128, false, f16_t, 4>(a, num_seqs, max_seqlen_q, stream)
                                 : dispatch_nh<128, false, f16_t, 8>(a, num_seqs, max_seqlen_q, stream))
@@ -1011,7 +1026,8 @@ hipError_t launch_prefill_mfma_int8(const void *q, int64_t q_row_stride, int hq,
     a.scale_log2 = softmax_scale * kLog2eF;
     a.out = reinterpret_cast<uint16_t *>(out);
     if (max_seqlen_q <= 0) return hipSuccess;
-    const bool w4 = prefill_grid(a.group, a.hkv, num_seqs, max_seqlen_q) > kNumCUs;  // as for 16-bit pools
+    bool w4;
+    plan_prefill(a, num_seqs, max_seqlen_q, w4);  // as for 16-bit pools
     if (q_dtype == 3)  // fp16 queries: the codes dequantize to fp16, fp16 MFMA
         return g.d == 128 ? (w4 ? dispatch_nh<128, true, f16_t, 4>(a, num_seqs, max_seqlen_q, stream)
                                 : dispatch_nh<128, true, f16_t, 8>(a, num_seqs, max_seqlen_q, stream))
