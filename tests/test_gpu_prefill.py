@@ -46,7 +46,9 @@ def test_c1_tiny_fp32():
     pre, _ = W.c1_tiny()
     say("[prefill] c1 fp32")
     got, ref, _ = run_prefill(pre)
-    assert max_abs_err(got, ref) <= tol("f32")
+    err = max_abs_err(got, ref)
+    say(f"  max-abs {err:.3e}")
+    assert err <= tol("f32")
 
 
 @pytest.mark.parametrize("n", [32, 128, 256])
@@ -65,7 +67,9 @@ def test_c3_prefix_suffix_and_full_rows():
     case = W.c3_prefix()
     say("[prefill] c3 prefix")
     got, ref, (kp, vp, kd, vd, out) = run_prefill(case)
-    assert max_abs_err(got, ref) <= tol("bf16")
+    err = max_abs_err(got, ref)
+    say(f"  max-abs {err:.3e}")
+    assert err <= tol("bf16")
     # full prefill of the same 300 tokens (queries of the cached part drawn fresh)
     rng = np.random.default_rng(1)
     q_full = W.normal(rng, (600, 16, 128), "bf16")
@@ -94,7 +98,9 @@ def test_c5a_mixed_chunked_sampled_rows():
     rows = sample_rows(case, 160, 5192)
     say(f"[prefill] c5a mixed {case.num_seqs} seqs, {len(rows)} sampled rows")
     got, ref, _ = run_prefill(case, rows=rows)
-    assert max_abs_err(got, ref) <= tol("bf16")
+    err = max_abs_err(got, ref)
+    say(f"  max-abs {err:.3e}")
+    assert err <= tol("bf16")
 
 
 @pytest.mark.parametrize("dtype,d,hq,hkv,bs", [
