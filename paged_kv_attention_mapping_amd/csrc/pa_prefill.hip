@@ -48,10 +48,11 @@
 //  * softmax runs against a running reference max that moves only when a
 //    block's probabilities would grow too large (see attend_tile), so the hot
 //    path computes no per-tile max.
-//  * a workgroup processes a PAIR of query tiles of one sequence, tile p and
-//    tile T-1-p, so every workgroup of a sequence does the same causal work;
-//    a launch whose single tiles all fit the CUs at once takes one tile per
-//    workgroup, so its time is one tile's latency chain instead of two.
+//  * a long prompt (one round of 8-wave workgroups) gives each workgroup a
+//    PAIR of query tiles of one sequence, tile p and tile T-1-p, so every
+//    workgroup of the sequence does the same causal work; other launches give
+//    each workgroup one tile, longest tiles dispatched first (see
+//    plan_prefill).
 //  * the KV head index varies fastest across workgroups; with 8 KV heads and
 //    workgroups dealt round-robin to the 8 XCDs, all tiles of one KV head run
 //    on one XCD and re-read its K/V from that XCD's L2.
@@ -173,6 +174,7 @@ struct PfArgs {
     const int32_t *cu_q;
     const int32_t *cu_k;
     const int32_t *q_off;
+    int num_seqs;
     int units_per_seq;      // work units (tile pairs, or single tiles) per sequence
     int single;             // 1: a unit is one query tile; 0: the pair (p, T-1-p)
     int total_q;            // rows of q and out: packed rows past it are never touched
@@ -669,8 +671,11 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void prefill_mfma_kernel(
     wg /= a.hkv;
     const int hgrp = (int)(wg % a.head_groups);
     wg /= a.head_groups;
-    const int pair = (int)(wg % a.units_per_seq);
-    const int s = (int)(wg / a.units_per_seq);
+    // single tiles: unit u of every sequence before unit u + 1, unit u being
+    // tile T-1-u, so the longest tiles of the batch are dispatched first;
+    // pairs: sequence-major
+    const int pair = (int)(a.single ? wg / a.num_seqs : wg % a.units_per_seq);
+    const int s = (int)(a.single ? wg % a.num_seqs : wg / a.units_per_seq);
 
     // rows outside [0, total_q) are never read or written, whatever cu_seqlens_q holds
     const int q_start = min(max(a.cu_q[s], 0), a.total_q);
@@ -725,7 +730,7 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void prefill_mfma_kernel(
     float *merge = reinterpret_cast<float *>(s_mem) + wl * (C::MERGE * 64);
 
     for (int it = 0; it < 2; ++it) {
-        const int tile = a.single ? pair : (it == 0 ? T - 1 - pair : pair);
+        const int tile = (a.single || it == 0) ? T - 1 - pair : pair;
         if (it == 1 && (a.single || tile == T - 1 - pair)) break;
 
         const int i_wg0 = tile * C::BM;
@@ -902,6 +907,7 @@ hipError_t run(const PfArgs &a, int num_seqs, int max_seqlen_q, hipStream_t stre
     using C = Pf<D, NH, E, NW>;
     PfArgs b = a;
     const int max_tiles = (max_seqlen_q + C::BM - 1) / C::BM;
+    b.num_seqs = num_seqs;
     b.units_per_seq = a.single ? max_tiles : (max_tiles + 1) / 2;
     b.head_groups = a.group / NH;
     const int64_t wgs = (int64_t)num_seqs * b.units_per_seq * b.head_groups * a.hkv;
@@ -931,19 +937,27 @@ int64_t prefill_grid(int group, int hkv, int num_seqs, int max_seqlen_q, bool si
     return (int64_t)num_seqs * (single ? tiles : (tiles + 1) / 2) * (group / nh) * hkv;
 }
 
-// Work units and layout of a launch.  Pairs of query tiles (p, T-1-p) give
-// every workgroup of a sequence the same causal work, which balances launches
-// of more than one round of workgroups.  A launch whose single tiles all fit
-// the CUs at once (short prompts, small batches) takes one tile per
-// workgroup instead: its time is then one tile's latency chain (metadata,
-// block ids, first keys, epilogue), not two in a row.  Layout: the 8-wave
-// workgroup while the launch fits the CUs in one round (every workgroup
-// streams its keys alone on a CU); the 4-wave one, two per CU, once there are
-// more workgroups than CUs (many or short sequences), so one workgroup's
-// prologue and epilogue overlap another's matrix work.
+// Work units and layout of a launch.
+//  * Layout: the 8-wave workgroup while the launch's tile pairs fit the CUs in
+//    one round (every workgroup streams its keys alone on a CU); the 4-wave
+//    one, two per CU, once they do not (many or short sequences), so one
+//    workgroup's prologue and epilogue overlap another's matrix work.
+//  * Units: pairs of query tiles (p, T-1-p) give the workgroups of a
+//    sequence equal causal work; they serve the one case where equal work
+//    matters, a single round of 8-wave workgroups that single tiles would
+//    overflow (a long prompt).  Otherwise a workgroup takes one tile: when the
+//    tiles all fit the CUs at once, the launch then costs one tile's latency
+//    chain (metadata, block ids, first keys, epilogue) rather than two in a
+//    row; with more tiles than slots, the smaller units, longest first, fill
+//    the slots more evenly (4-wave layout, measured on MI355X: 8192 new
+//    tokens over 17 sequences of 35 to 842, 56 -> 45 us against tile pairs).
+//    Sequence-major single tiles keep a sequence's tiles together in L2 and
+//    were faster for 64 equal sequences of 128 tokens (28 against 35 us) but
+//    slower for the ragged batch (49 us).
 void plan_prefill(PfArgs &a, int num_seqs, int max_seqlen_q, bool &w4) {
-    a.single = prefill_grid(a.group, a.hkv, num_seqs, max_seqlen_q, true) <= kNumCUs ? 1 : 0;
+    const bool singles_fit = prefill_grid(a.group, a.hkv, num_seqs, max_seqlen_q, true) <= kNumCUs;
     w4 = prefill_grid(a.group, a.hkv, num_seqs, max_seqlen_q, false) > kNumCUs;
+    a.single = (singles_fit || w4) ? 1 : 0;
 }
 
 }  // namespace
