@@ -247,3 +247,22 @@ def test_many_short_sequences_two_workgroups_per_cu(dtype, d, hq, hkv, bs):
     err = max_abs_err(got, ref)
     say(f"  max-abs {err:.3e}")
     assert err <= tol(dtype)
+
+
+@pytest.mark.parametrize("q_lens,q_offs,units", [
+    ([1024, 1000], [0, 37], "single tiles that exactly fill the CUs (256 workgroups, 8-wave)"),
+    ([1000, 1024, 990, 1017], [0, 24, 3, 100], "tile pairs of several sequences (256 workgroups, 8-wave)"),
+    ([700, 64, 1024, 5, 300, 999], [0, 900, 0, 17, 0, 1], "single tiles longest first (4-wave)"),
+])
+def test_work_units_across_sequences(q_lens, q_offs, units):
+    """Each work-unit choice of the launch (pairs of query tiles, single tiles
+    fitting the CUs, single tiles dispatched longest first) over several
+    sequences with cached prefixes: sampled rows, every sequence's first and
+    last rows included, against the oracle."""
+    case = W.make_prefill("units", 9500 + len(q_lens), q_lens, q_offs, 16, 8, 128, 16, "bf16")
+    rows = sample_rows(case, 64, 9501)
+    say(f"[prefill] {units}: {len(rows)} sampled rows")
+    got, ref, _ = run_prefill(case, rows=rows)
+    err = max_abs_err(got, ref)
+    say(f"  max-abs {err:.3e}")
+    assert err <= tol("bf16")
