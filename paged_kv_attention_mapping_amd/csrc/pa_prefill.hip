@@ -549,9 +549,11 @@ struct SoftState {
 // if some lane's block sum exceeds kBlockSumMax (or no max is set yet) does
 // the wave take the cold path (rebase_block).  O / l is exact whatever the
 // reference is, since both use it.  Issue order: block 0's QK MFMAs; block
-// 1's QK MFMAs, with block 0's exponentials after each; block 0's PV MFMAs,
-// each followed by two of block 1's exponentials and the V^T reads of block
-// 1; block 1's PV MFMAs (sched_barrier keeps the groups in that order).
+// 1's QK MFMAs, then block 0's exponentials (the compiler's order here: the
+// second wave of the SIMD fills the gap, and interleaving them one by one
+// measured no faster); block 0's PV MFMAs, each followed by two of block 1's
+// exponentials and the V^T reads of block 1; block 1's PV MFMAs
+// (sched_barrier keeps the groups in that order).
 template <class C>
 __device__ __forceinline__ void attend_tile(const unsigned char *kbuf, const unsigned char *vbuf,
                                             const int (&kofs)[C::KS], const int (&vofs)[C::DT],
