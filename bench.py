@@ -57,6 +57,9 @@ def parse():
     p.add_argument("--no-int8", action="store_true", help="skip the INT8 KV-cache measurements")
     p.add_argument("--no-f16", action="store_true", help="skip the fp16 measurements")
     p.add_argument("--no-graph", action="store_true", help="skip the HIP graph replay measurements")
+    p.add_argument("--no-small", action="store_true",
+                   help="skip the small-shape timings (they launch the long prompt's prefill kernel too, "
+                        "which would mix into a kernel trace's per-kernel statistics)")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="also run one plain 1 GiB device copy (HBM counter calibration)")
     return p.parse_args()
@@ -190,7 +193,7 @@ def main():
 
     graph = None if args.no_graph else graph_measure(step, ms_per_step, max(args.steps, 2))
     mixed = mixed_prefill_measure(pa, W, max(args.steps, 2))
-    small = small_configs_measure(pa, W)
+    small = None if args.no_small else small_configs_measure(pa, W)
 
     f16 = None if args.no_f16 else f16_measure(pa, W, lay, ctx_d, bt_d, order_d, dec_call_ms, pf_call_ms,
                                                max(args.steps, 2))
@@ -253,7 +256,8 @@ def main():
     if graph is not None:
         result["graph_step"] = graph
     result["prefill_mixed"] = mixed
-    result["small_configs"] = small
+    if small is not None:
+        result["small_configs"] = small
     print(json.dumps(result), flush=True)
 
 
