@@ -124,7 +124,8 @@ pa_status pa_store_kv(const void *k, int64_t k_row_stride,
  *   slot_mapping  int32 [num_tokens]; -1 = padding token, skipped.
  *   k_pool,v_pool int8 code pools, 8-byte aligned; k_scale,v_scale fp16
  *                 scale pools; all written in place.
- *   pool          dtype PA_INT8; head_dim a multiple of 8, at most 256.
+ *   pool          dtype PA_INT8; head_dim a power of two from 8 to 256 (a
+ *                 head vector's lanes reduce its max |x| as one group).
  * Errors: PA_ERR_BAD_DTYPE (pool not PA_INT8, src_dtype not bf16/fp16/fp32),
  * PA_ERR_UNSUPPORTED (head_dim, block_size, misaligned pools), the checks of
  * pa_store_kv otherwise.  Slots must be unique within one call.

@@ -77,6 +77,20 @@ void say(char *why, size_t why_len, const char *fmt, long long a, long long b) {
     if (why && why_len) snprintf(why, why_len, fmt, a, b);
 }
 
+// INT8 decode: the float decode's checks, with int8 code pools, fp16 scale
+// pools and q / out of q_dtype; query groups of 1, 2, 4 or 8.
+pa_status check_decode_int8_shape(const pa_pool *pool, int32_t num_q_heads, int32_t q_dtype, pa::PoolGeom *g) {
+    pa_status st = check_pool_int8(pool, g);
+    if (st != PA_OK) return st;
+    if (!float_dtype(q_dtype)) return PA_ERR_BAD_DTYPE;
+    if (num_q_heads <= 0 || num_q_heads % g->hkv) return PA_ERR_BAD_SHAPE;
+    const int group = num_q_heads / g->hkv;
+    if (group != 1 && group != 2 && group != 4 && group != 8) return PA_ERR_UNSUPPORTED;
+    if (g->d != 32 && g->d != 64 && g->d != 128 && g->d != 256) return PA_ERR_UNSUPPORTED;
+    if (g->num_blocks < 1) return PA_ERR_BAD_SHAPE;
+    return PA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -120,7 +134,9 @@ pa_status pa_store_kv_int8(const void *k, int64_t k_row_stride, const void *v, i
     if (st != PA_OK) return st;
     if (!float_dtype(src_dtype)) return PA_ERR_BAD_DTYPE;
     if (num_tokens < 0) return PA_ERR_BAD_SHAPE;
-    if (g.d % 8 || g.d > 256) return PA_ERR_UNSUPPORTED;
+    // a head vector is d/8 (16-bit rows) or d/4 (fp32 rows) lanes that reduce
+    // max |x| with xor shuffles: the group must be a power of two
+    if (g.d < 8 || g.d > 256 || !is_pow2(g.d)) return PA_ERR_UNSUPPORTED;
     if (num_tokens == 0) return PA_OK;
     if (!k || !v || !slot_mapping || !k_pool || !v_pool || !k_scale || !v_scale) return PA_ERR_NULL_ARG;
     const int64_t row = (int64_t)g.hkv * g.d;
@@ -242,20 +258,6 @@ pa_status pa_decode(const void *q, int64_t q_row_stride, int32_t num_q_heads, co
     return from_hip(pa::launch_decode(q, q_row_stride, num_q_heads, k_pool, v_pool, g, context_lens,
                                       block_table, block_table_stride, plan, softmax_scale, row_order,
                                       out, workspace, (hipStream_t)stream));
-}
-
-// INT8 decode: the float decode's checks, with int8 code pools, fp16 scale
-// pools and q / out of q_dtype; query groups of 1, 2, 4 or 8.
-pa_status check_decode_int8_shape(const pa_pool *pool, int32_t num_q_heads, int32_t q_dtype, pa::PoolGeom *g) {
-    pa_status st = check_pool_int8(pool, g);
-    if (st != PA_OK) return st;
-    if (!float_dtype(q_dtype)) return PA_ERR_BAD_DTYPE;
-    if (num_q_heads <= 0 || num_q_heads % g->hkv) return PA_ERR_BAD_SHAPE;
-    const int group = num_q_heads / g->hkv;
-    if (group != 1 && group != 2 && group != 4 && group != 8) return PA_ERR_UNSUPPORTED;
-    if (g->d != 32 && g->d != 64 && g->d != 128 && g->d != 256) return PA_ERR_UNSUPPORTED;
-    if (g->num_blocks < 1) return PA_ERR_BAD_SHAPE;
-    return PA_OK;
 }
 
 size_t pa_decode_int8_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,

@@ -221,7 +221,7 @@ hipError_t launch_store_kv_int8(const void *k, int64_t k_row_stride, const void 
     if (num_tokens == 0) return hipSuccess;
     const int eb = src_dtype == 0 ? 4 : 2;
     const int E = 16 / eb;
-    const int lanes = g.d / E;  // head_dim is a multiple of 8 and at most 512 (checked by the caller)
+    const int lanes = g.d / E;  // a power of two, at most 64: head_dim is one from 8 to 256 (checked by the caller)
     const int64_t vectors = (int64_t)num_tokens * g.hkv;
     const int64_t threads = vectors * lanes;
     const unsigned grid = (unsigned)((threads + kStoreThreads - 1) / kStoreThreads);

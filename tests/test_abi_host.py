@@ -33,13 +33,28 @@ def test_library_loads_and_exports_every_symbol():
     assert b"workspace" in lib.pa_status_string(5)
 
 
+def test_library_exports_exactly_the_header():
+    """The dynamic symbol table of libpa.so defines the C entry points that
+    include/pa.h declares and no other symbol (no helper, no C++ name)."""
+    import subprocess
+    res = subprocess.run(["nm", "-D", "--defined-only", pa.LIB_PATH], capture_output=True, text=True,
+                         check=True)
+    exported = set()
+    for line in res.stdout.splitlines():
+        parts = line.split()
+        if len(parts) == 3 and parts[1] in "TtDdBbRrVvWwiu" and not parts[2].startswith("PA_"):
+            exported.add(parts[2])
+    assert exported == _declared_symbols(), sorted(exported ^ _declared_symbols())
+
+
 def _pool(nb=4, bs=16, hkv=2, d=32, dtype=pa.PA_F32):
     return pa.PaPool(nb, bs, hkv, d, dtype)
 
 
 def test_int8_store_host_errors():
     """pa_store_kv_int8 takes PA_INT8 pools only (and the bf16/fp32 calls
-    refuse them), bf16 or fp32 sources, head_dim a multiple of 8."""
+    refuse them), bf16, fp16 or fp32 sources, head_dim a power of two from 8 to 256
+    (the lanes of a head vector reduce its max |x| as one group)."""
     lib = pa.load()
     i8 = _pool(d=128, dtype=pa.PA_INT8)
     dummy = ctypes.c_void_p(4096)
@@ -48,8 +63,9 @@ def test_int8_store_host_errors():
     assert lib.pa_store_kv_int8(*a) == 3                       # pool not INT8
     a = list(args); a[4] = pa.PA_INT8
     assert lib.pa_store_kv_int8(*a) == 3                       # source must be bf16 / fp16 / fp32
-    a = list(args); a[11] = ctypes.byref(_pool(d=36, dtype=pa.PA_INT8))
-    assert lib.pa_store_kv_int8(*a) == 4                       # head_dim % 8
+    for d in (36, 24, 40, 48, 96, 4, 512):
+        a = list(args); a[11] = ctypes.byref(_pool(d=d, dtype=pa.PA_INT8))
+        assert lib.pa_store_kv_int8(*a) == 4, d                # head_dim not a power of two in 8..256
     a = list(args); a[6] = 0
     assert lib.pa_store_kv_int8(*a) == 0                       # no tokens: no-op
     a = list(args); a[9] = None

@@ -1,6 +1,6 @@
 """pa_decode on the GPU against the fp64 oracle: C1's decode steps, C4 (256
 sequences x U[100,2048], one layer pool in full plus a second layer), C5b
-(64 x 32768, sampled sequences) and edge cases."""
+(64 x 32768, every row) and edge cases."""
 import numpy as np
 import pytest
 import torch
@@ -92,30 +92,30 @@ def test_c4_batch_decode_full_layer():
     assert err <= tol("bf16")
 
 
-def test_c4_second_layer_pool_sampled():
+def test_c4_second_layer_pool_every_row():
     lay = W.c4_decode_layout()
-    say("[decode] c4 layer 27 sampled")
+    say("[decode] c4 layer 27, every row")
     q, kd, vd = _device_layer(lay, 27)
     out = pa.pa_decode(q, kd, vd, to_dev(lay.context_lens), to_dev(lay.block_table), lay.max_context_len,
                        lay.scale)
     torch.cuda.synchronize()
-    seqs = np.array([0, 1, 77, 128, 200, 255], np.int32)
     ref = oracle.decode(to_host_bits(q), to_host_bits(kd), to_host_bits(vd), lay.context_lens,
-                        lay.block_table, lay.scale, seqs=seqs)
-    assert max_abs_err(out[torch.as_tensor(seqs, device="cuda").long()], ref) <= tol("bf16")
+                        lay.block_table, lay.scale)
+    err = max_abs_err(out, ref)
+    say(f"  max-abs {err:.3e}")
+    assert err <= tol("bf16")
 
 
-def test_c5b_long_context_sampled():
+def test_c5b_long_context_every_row():
     lay = W.c5b_decode_layout()
-    say("[decode] c5b 64 x 32768 (sampled sequences)")
+    say("[decode] c5b 64 x 32768, every row")
     q, kd, vd = _device_layer(lay, 0)
     out = pa.pa_decode(q, kd, vd, to_dev(lay.context_lens), to_dev(lay.block_table), lay.max_context_len,
                        lay.scale)
     torch.cuda.synchronize()
-    seqs = np.array([0, 31, 63], np.int32)
     ref = oracle.decode(to_host_bits(q), to_host_bits(kd), to_host_bits(vd), lay.context_lens,
-                        lay.block_table, lay.scale, seqs=seqs)
-    err = max_abs_err(out[torch.as_tensor(seqs, device="cuda").long()], ref)
+                        lay.block_table, lay.scale)
+    err = max_abs_err(out, ref)
     say(f"  max-abs {err:.3e}")
     assert err <= tol("bf16")
     again = pa.pa_decode(q, kd, vd, to_dev(lay.context_lens), to_dev(lay.block_table), lay.max_context_len,

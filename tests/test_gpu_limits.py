@@ -32,7 +32,7 @@ def _decode(case, row_order=True):
 def test_block_size_65536_decode_and_prefill():
     """Blocks of 65536 tokens: rows of 70000 and 65536 keys (across and at a
     block boundary) decode; a 96-token chunk after a 69904-token prefix
-    prefills on the matrix cores (sampled rows)."""
+    prefills on the matrix cores (every row)."""
     bs = 65536
     dec = W.make_decode("bs64k", 9400, [70000, 65536, 3], 4, 2, 128, bs, "bf16", num_spare=1)
     say("[limits] decode, block size 65536")
@@ -52,9 +52,8 @@ def test_block_size_65536_decode_and_prefill():
     got = pa.pa_prefill_varlen(to_dev(pf.q), kd, vd, to_dev(pf.cu_seqlens_q), to_dev(pf.cu_seqlens_k), to_dev(offs),
                                to_dev(pf.block_table), pf.max_seqlen_q, pf.max_seqlen_k, pf.scale)
     torch.cuda.synchronize()
-    rows = np.array([0, 1, 31, 32, 63, 64, 95], np.int32)
-    ref = oracle.prefill(pf.q, kp, vp, pf.cu_seqlens_q, pf.cu_seqlens_k, offs, pf.block_table, pf.scale, rows=rows)
-    err = max_abs_err(got[torch.as_tensor(rows, device="cuda").long()], ref)
+    ref = oracle.prefill(pf.q, kp, vp, pf.cu_seqlens_q, pf.cu_seqlens_k, offs, pf.block_table, pf.scale)
+    err = max_abs_err(got, ref)
     say(f"  max-abs {err:.3e}")
     assert err <= tol("bf16")
 
@@ -91,9 +90,8 @@ def test_decode_4096_rows_without_row_order():
     dec = W.make_decode("rows4096", 9420, ctx, 16, 8, 64, 32, "bf16")
     say("[limits] decode 4096 rows")
     out, kp, vp = _decode(dec, row_order=False)
-    rows = np.unique(np.concatenate([np.arange(8), np.arange(4088, 4096), rng.choice(4096, 64, replace=False)]))
-    ref = oracle.decode(dec.q, kp, vp, dec.context_lens, dec.block_table, dec.scale, seqs=rows.astype(np.int32))
-    assert max_abs_err(out[torch.as_tensor(rows, device="cuda").long()], ref) <= tol("bf16")
+    ref = oracle.decode(dec.q, kp, vp, dec.context_lens, dec.block_table, dec.scale)
+    assert max_abs_err(out, ref) <= tol("bf16")
     zero = np.nonzero(ctx == 0)[0]
     assert (to_host_bits(out)[zero] == 0).all()
 

@@ -170,6 +170,41 @@ def test_decode_equals_last_row_of_prefill():
     assert o_dec.tobytes() == o_full[last].tobytes()
 
 
+def test_row_subset_equals_rows_of_the_full_prefill():
+    """The oracle's rows= path (rows in any order, repeated, from several
+    sequences, with cached prefixes and a zero-length sequence) returns, bit
+    for bit, the same rows of the full output; its pair count is theirs."""
+    case = W.make_prefill("subset", 81, [37, 0, 5, 64, 1], [0, 9, 20, 3, 70], 4, 2, 16, 8, "bf16")
+    kp, vp = _case_pools(case)
+    full, full_pairs = oracle.prefill(case.q, kp, vp, case.cu_seqlens_q, case.cu_seqlens_k, case.q_offsets,
+                                      case.block_table, case.scale, return_pairs=True)
+    assert full_pairs == case.causal_pairs
+    rows = np.array([106, 0, 41, 36, 41, 37, 42, 105, 5], np.int32)
+    sub, pairs = oracle.prefill(case.q, kp, vp, case.cu_seqlens_q, case.cu_seqlens_k, case.q_offsets,
+                                case.block_table, case.scale, rows=rows, return_pairs=True)
+    assert sub.tobytes() == full[rows].tobytes()
+    cu = np.asarray(case.cu_seqlens_q)
+    seq_of = np.searchsorted(cu, rows, side="right") - 1
+    visible = [min(case.q_offsets[s] + r - cu[s], case.k_lens[s] - 1) + 1 for r, s in zip(rows, seq_of)]
+    assert pairs == sum(visible)
+
+
+def test_sequence_subset_equals_rows_of_the_full_decode():
+    """The oracle's seqs= path returns, bit for bit, the same rows of the full
+    decode output (a padding row of context 0 included)."""
+    case = W.make_decode("subset", 82, [9, 0, 33, 1, 200, 17], 4, 2, 16, 8, "f32")
+    kp, vp = case.empty_pools()
+    oracle.store_kv(case.k_hist, case.v_hist, case.slot_hist, kp, vp)
+    oracle.store_kv(case.k_new, case.v_new, case.slot_new, kp, vp)
+    full = oracle.decode(case.q, kp, vp, case.context_lens, case.block_table, case.scale)
+    seqs = np.array([4, 1, 0, 4, 5, 2], np.int32)
+    sub, pairs = oracle.decode(case.q, kp, vp, case.context_lens, case.block_table, case.scale, seqs=seqs,
+                               return_pairs=True)
+    assert sub.tobytes() == full[seqs].tobytes()
+    assert pairs == int(np.asarray(case.context_lens)[seqs].sum())
+    assert (sub[1] == 0).all()
+
+
 def test_block_permutation_invariance():
     """Only the block table says where a block lives: relabelling physical
     blocks (and the table with them) gives bit-identical results."""
