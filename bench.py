@@ -62,6 +62,10 @@ def parse():
                         "which would mix into a kernel trace's per-kernel statistics)")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="also run one plain 1 GiB device copy (HBM counter calibration)")
+    p.add_argument("--no-c5b", action="store_true", help="skip the 64 x 32768 long-context decode")
+    p.add_argument("--only-c5b", action="store_true",
+                   help="run only the 64 x 32768 long-context decode (for a kernel trace of that shape alone); "
+                        "prints its JSON block")
     return p.parse_args()
 
 
@@ -79,6 +83,14 @@ def main():
 
     torch.cuda.set_device(0)
     dev = "cuda"
+    if args.only_c5b:
+        res = c5b_measure(pa, W, max(args.steps, 2))
+        if args.calibrate_copy:
+            src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+            torch.empty_like(src).copy_(src)
+            torch.cuda.synchronize()
+        print(json.dumps({"decode_c5b": res}), flush=True)
+        return
 
     def to_dev(a):
         if a.dtype == np.uint16:
@@ -197,10 +209,11 @@ def main():
 
     f16 = None if args.no_f16 else f16_measure(pa, W, lay, ctx_d, bt_d, order_d, dec_call_ms, pf_call_ms,
                                                max(args.steps, 2))
+    c5b = None if args.no_c5b else c5b_measure(pa, W, max(args.steps, 2))
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(lay, k_pools[0], v_pools[0], qs[0])
+        cpu = cpu_baseline(lay, k_pools[0], v_pools[0], qs[0], pf, pf_k, pf_v, pf_q)
 
     result = {
         "metric": "paged-attn decode KV GB/s + prefill TFLOP/s (Qwen3-0.6B shapes, 1 GPU)",
@@ -215,6 +228,15 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) K/V/Q; seeded lengths and shuffled block tables)",
+        "seeds": {
+            "prefill_1x4096": {"lengths_table_values": pf.seed},
+            "decode_256": {"lengths_table": lay.seed, "k_pool_layer_l": "4100+2l", "v_pool_layer_l": "4101+2l",
+                           "q_layer_l": "9000+l", "new_k_layer_l": "7000+2l", "new_v_layer_l": "7001+2l"},
+            "decode_64x32768": {"lengths_table": W.c5b_decode_layout().seed, "k_pool": 5330, "v_pool": 5331,
+                                "q": 5332},
+            "prefill_mixed_8192": {"lengths_table": W.c5a_mixed(with_values=False).seed, "k_pool": 5400,
+                                   "v_pool": 5401, "q": 5402},
+        },
         "config": {
             "workload": (f"qwen3-0.6b attention step: store+prefill 1x4096 causal (block 16) + "
                          f"{L} layers x (store 256 + decode 256 seqs, ctx U[100,2048], block 256)"),
@@ -253,6 +275,8 @@ def main():
         result.update(int8)
     if f16 is not None:
         result.update(f16)
+    if c5b is not None:
+        result["decode_c5b"] = c5b
     if graph is not None:
         result["graph_step"] = graph
     result["prefill_mixed"] = mixed
@@ -408,6 +432,39 @@ def mixed_prefill_measure(pa, W, reps):
             "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
                          "traffic": measured_traffic("prefill_mixed")}}
+
+
+def c5b_measure(pa, W, reps):
+    """Long-context decode: 64 sequences x 32768 keys (block 16, one layer
+    pool, 8.59 GB of K/V), one pa_decode call per launch (not part of the
+    step).  Bytes: every visible K and V row once per KV head."""
+    import torch
+    dev = "cuda"
+    lay = W.c5b_decode_layout()
+    nb, bs, hkv, d, hq = lay.num_blocks, lay.block_size, lay.num_kv_heads, lay.head_dim, lay.num_q_heads
+    kp = W.device_normal((nb, bs, hkv, d), 5330)
+    vp = W.device_normal((nb, bs, hkv, d), 5331)
+    q = W.device_normal((lay.num_seqs, hq, d), 5332)
+    out = torch.empty_like(q)
+    i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)  # noqa: E731
+    ctx, bt = i32(lay.context_lens), i32(lay.block_table)
+    ws = torch.empty(max(pa.pa_decode_workspace_bytes(lay.num_seqs, hq, lay.max_context_len, kp), 1),
+                     dtype=torch.uint8, device=dev)
+    order = pa.pa_decode_order(ctx)
+    ms = _time_calls([lambda: pa.pa_decode(q, kp, vp, ctx, bt, lay.max_context_len, lay.scale, out=out,
+                                           workspace=ws, row_order=order)], max(reps, 5))
+    kv = lay.kv_bytes()
+    gbps = kv / (ms * 1e-3) / 1e9
+    del kp, vp
+    torch.cuda.empty_cache()
+    return {"value": round(gbps, 2), "unit": "GB/s",
+            "workload": (f"decode {lay.num_seqs} seqs x {int(lay.context_lens[0])} keys, block {bs}, "
+                         f"{hq}/{hkv} heads, d {d}, bf16, one layer pool"),
+            "avg_launch_us": round(ms * 1e3, 2), "bytes_per_launch": kv,
+            "roofline": {"bound": "hbm",
+                         "kernel": "pa_decode (split-K kernel + log-sum-exp merge)",
+                         "achieved": round(gbps, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                         "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": measured_traffic("decode_c5b")}}
 
 
 def _time_in_graph(fn, calls=20, replays=5):
@@ -635,10 +692,26 @@ def measured_traffic(which):
     return int(rec["read_bytes"] + rec["write_bytes"])
 
 
-def cpu_baseline(lay, k_pool, v_pool, q, target_s=12.0):
-    """The fp64 CPU oracle, on host cores, over a bounded sample of the decode
-    workload: layer 0 (all 256 sequences, all 16 query heads), repeated until
-    about target_s seconds of host work have run."""
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(lay, k_pool, v_pool, q, pf, pf_k, pf_v, pf_q, target_s=10.0):
+    """The fp64 CPU oracle on the host cores, over bounded samples of the
+    same workloads (a reported baseline, not a target):
+      * decode layer 0 (all 256 sequences, all 16 query heads), repeated
+        until about target_s seconds of host work have run on all threads,
+        then once on a single thread over its first 32 sequences;
+      * the 1 x 4096 prefill over every 4th query row on all threads, and
+        over every 64th row on a single thread.
+    Rates are in the metric's units (decode: KV bytes per second; prefill:
+    4*d*Hq FLOP per visible causal pair per second, fp64)."""
     import torch
 
     import oracle
@@ -646,6 +719,7 @@ def cpu_baseline(lay, k_pool, v_pool, q, target_s=12.0):
     def bits(t):
         return t.cpu().view(torch.int16).numpy().view(np.uint16)
 
+    threads = oracle.num_threads()
     kp, vp, qh = bits(k_pool), bits(v_pool), bits(q)
     reps, t_total = 0, 0.0
     while t_total < target_s and reps < 1000:
@@ -654,10 +728,45 @@ def cpu_baseline(lay, k_pool, v_pool, q, target_s=12.0):
         t_total += time.perf_counter() - t0
         reps += 1
     kv = lay.kv_bytes() * reps
-    return {"value": round(kv / t_total / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(),
+    d, hq, hkv = lay.head_dim, lay.num_q_heads, lay.num_kv_heads
+    dec_flops = 4.0 * d * hq * float(lay.context_lens.astype(np.int64).sum()) * reps
+    seqs1 = np.arange(32, dtype=np.int32)
+    oracle.set_num_threads(1)
+    try:
+        t0 = time.perf_counter()
+        oracle.decode(qh, kp, vp, lay.context_lens, lay.block_table, lay.scale, seqs=seqs1)
+        t1_dec = time.perf_counter() - t0
+        kv1 = int(lay.context_lens[:32].astype(np.int64).sum()) * hkv * d * 2 * 2
+
+        pkp, pvp, pqh = bits(pf_k), bits(pf_v), bits(pf_q)
+        rows1 = np.arange(0, pf.total_q, 64, dtype=np.int32)
+        t0 = time.perf_counter()
+        _, pairs1 = oracle.prefill(pqh, pkp, pvp, pf.cu_seqlens_q, pf.cu_seqlens_k, pf.q_offsets, pf.block_table,
+                                   pf.scale, rows=rows1, return_pairs=True)
+        t1_pf = time.perf_counter() - t0
+    finally:
+        oracle.set_num_threads(threads)
+    rows = np.arange(0, pf.total_q, 4, dtype=np.int32)
+    t0 = time.perf_counter()
+    _, pairs = oracle.prefill(pqh, pkp, pvp, pf.cu_seqlens_q, pf.cu_seqlens_k, pf.q_offsets, pf.block_table,
+                              pf.scale, rows=rows, return_pairs=True)
+    t_pf = time.perf_counter() - t0
+    pf_flops, pf_flops1 = 4.0 * d * hq * pairs, 4.0 * d * hq * pairs1
+    return {"value": round(kv / t_total / 1e9, 4), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
-            "sample": (f"decode layer 0 ({lay.num_seqs} sequences, {lay.num_q_heads} query heads, "
-                       f"{lay.kv_bytes()} KV bytes) x {reps} repetitions, {t_total:.1f} s fp64")}
+            "sample": (f"decode layer 0 ({lay.num_seqs} sequences, {hq} query heads, "
+                       f"{lay.kv_bytes()} KV bytes) x {reps} repetitions, {t_total:.1f} s fp64 on {threads} threads"),
+            "cpu_model": _cpu_model(),
+            "decode_fp64_gflops": round(dec_flops / t_total / 1e9, 3),
+            "decode_one_thread": {"value": round(kv1 / t1_dec / 1e9, 4), "unit": "GB/s",
+                                  "sample": f"decode layer 0, sequences 0..31 ({kv1} KV bytes), {t1_dec:.1f} s"},
+            "prefill": {"value": round(pf_flops / t_pf / 1e9, 3), "unit": "GFLOP/s", "cores": threads,
+                        "sample": (f"prefill 1x4096 causal, every 4th query row ({len(rows)} rows x {hq} heads, "
+                                   f"{pairs} causal pairs), {t_pf:.1f} s fp64"),
+                        "full_prefill_s_estimate": round(t_pf * 4.0, 2)},
+            "prefill_one_thread": {"value": round(pf_flops1 / t1_pf / 1e9, 3), "unit": "GFLOP/s",
+                                   "sample": (f"prefill 1x4096 causal, every 64th query row ({len(rows1)} rows, "
+                                              f"{pairs1} causal pairs), {t1_pf:.1f} s fp64")}}
 
 
 if __name__ == "__main__":

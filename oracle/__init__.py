@@ -8,6 +8,7 @@ from .oracle import (  # noqa: F401
     build,
     lib_path,
     num_threads,
+    set_num_threads,
     store_kv,
     gather_kv,
     prefill,

@@ -49,6 +49,8 @@ def _load():
         lib = ctypes.CDLL(_LIB)
         p, i32, i64, f64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_double
         lib.oracle_num_threads.restype = ctypes.c_int
+        lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
+        lib.oracle_set_num_threads.restype = ctypes.c_int
         lib.oracle_store_kv.argtypes = [p, i64, p, i64, p, i32, p, p, i64, i32, i32, i32, i32]
         lib.oracle_gather_kv.argtypes = [p, p, i64, i32, i32, i32, i32, p, p, i32, i32, p, p]
         lib.oracle_prefill.argtypes = [p, i64, i32, i32, p, p, i64, i32, i32, i32,
@@ -86,6 +88,11 @@ def _i32(a) -> np.ndarray:
 
 def num_threads() -> int:
     return int(_load().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> int:
+    """Host threads of the attention loops from now on (timing only); returns the number in effect."""
+    return int(_load().oracle_set_num_threads(int(n)))
 
 
 def store_kv(k, v, slot_mapping, k_pool, v_pool) -> None:

@@ -92,6 +92,19 @@ int oracle_num_threads(void)
 #endif
 }
 
+/* Host threads the attention loops use from now on (n >= 1); returns the
+ * number in effect.  Timing only: results do not depend on it. */
+int oracle_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+    return omp_get_max_threads();
+#else
+    (void)n;
+    return 1;
+#endif
+}
+
 /*
  * Store: for every token t whose slot is not -1, copy its K row and V row
  * (num_kv_heads * head_dim elements, taken at t * row_stride elements) to
