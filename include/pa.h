@@ -13,8 +13,9 @@
  *    the caller and must stay alive until the work enqueued on `stream`
  *    completes.  `stream` is a hipStream_t (NULL = the default stream).
  *  - Calls only enqueue work on `stream`: no device synchronisation, no
- *    device-to-host copy, no allocation, no global mutable state.  They may
- *    be called from several host threads and captured in a HIP graph.
+ *    device-to-host copy, no allocation, no global mutable state (except
+ *    pa_decode_static's per-GPU scratch array, see there).  They may be
+ *    called from several host threads and captured in a HIP graph.
  *  - Errors: a pa_status is returned synchronously for problems visible on
  *    the host (null pointers, sizes, unsupported shapes, a workspace that is
  *    too small) and nothing is enqueued.  PA_ERR_HIP means a launch failed
@@ -55,7 +56,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 4
+#define PA_ABI_VERSION 5
 
 typedef enum {
     PA_OK = 0,
@@ -293,6 +294,31 @@ pa_status pa_decode(const void *q, int64_t q_row_stride, int32_t num_q_heads,
                     int32_t block_table_stride, int32_t num_seqs, int32_t max_context_len,
                     float softmax_scale, const int32_t *row_order, void *out, void *workspace,
                     size_t workspace_bytes, void *stream);
+
+/*
+ * pa_decode_static -- pa_decode without a caller workspace, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation).  It computes pa_decode's result
+ * with the same kernels and the same split plan; the split-K partials go to a
+ * device array the library defines at file scope, 16 MiB per GPU (held by
+ * each GPU the library runs on until the process ends).  Its address on the
+ * current device is looked up once per device (hipGetSymbolAddress, no
+ * allocation); the call itself allocates and frees nothing.
+ *
+ * Arguments as pa_decode, minus workspace and workspace_bytes.
+ * Errors: those of pa_decode; PA_ERR_WORKSPACE when the partials this call
+ * needs (pa_decode_workspace_bytes with the same sizes) exceed 16 MiB,
+ * returned before any device call; PA_ERR_HIP if the lookup fails.
+ * Every call on one GPU shares that GPU's array and leaves its partials in
+ * it: calls that overlap on one GPU (several streams or host threads at once)
+ * race and give wrong results; calls ordered on one stream are safe.  The
+ * array needs no clearing: each call writes every partial it reads.
+ */
+pa_status pa_decode_static(const void *q, int64_t q_row_stride, int32_t num_q_heads,
+                           const void *k_pool, const void *v_pool, const pa_pool *pool /* host */,
+                           const int32_t *context_lens, const int32_t *block_table,
+                           int32_t block_table_stride, int32_t num_seqs, int32_t max_context_len,
+                           float softmax_scale, const int32_t *row_order, void *out, void *stream);
 
 /*
  * pa_decode_order -- scheduling aid for pa_decode, not an operation of the

@@ -17,6 +17,7 @@ from ._lib import (  # noqa: F401
     load,
     pa_copy_blocks,
     pa_decode,
+    pa_decode_static,
     pa_decode_int8,
     pa_decode_int8_workspace_bytes,
     pa_decode_order,

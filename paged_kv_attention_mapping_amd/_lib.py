@@ -27,7 +27,7 @@ _STATUS = {
 
 # Every symbol include/pa.h declares.
 EXPORTS = (
-    "pa_store_kv", "pa_store_kv_int8", "pa_prefill_varlen", "pa_decode", "pa_decode_int8",
+    "pa_store_kv", "pa_store_kv_int8", "pa_prefill_varlen", "pa_decode", "pa_decode_static", "pa_decode_int8",
     "pa_decode_int8_workspace_bytes", "pa_prefill_varlen_int8", "pa_prefill_int8_workspace_bytes",
     "pa_decode_order", "pa_copy_blocks",
     "pa_prefill_workspace_bytes",
@@ -68,6 +68,7 @@ def load() -> ctypes.CDLL:
     lib.pa_prefill_varlen.argtypes = [p, i64, i32, p, p, pool, p, p, p, p, i32, i32, i32, i32, i32, f32,
                                       p, p, sz, p]
     lib.pa_decode.argtypes = [p, i64, i32, p, p, pool, p, p, i32, i32, i32, f32, p, p, p, sz, p]
+    lib.pa_decode_static.argtypes = [p, i64, i32, p, p, pool, p, p, i32, i32, i32, f32, p, p, p]
     lib.pa_decode_int8.argtypes = [p, i64, i32, i32, p, p, p, p, pool, p, p, i32, i32, i32, f32, p, p, p, sz, p]
     lib.pa_decode_int8_workspace_bytes.argtypes = [i32, i32, i32, pool]
     lib.pa_decode_int8_workspace_bytes.restype = sz
@@ -87,7 +88,7 @@ def load() -> ctypes.CDLL:
     lib.pa_status_string.restype = ctypes.c_char_p
     lib.pa_abi_version.restype = ctypes.c_int
     for fn in ("pa_store_kv", "pa_store_kv_int8", "pa_prefill_varlen", "pa_prefill_varlen_int8", "pa_decode",
-               "pa_decode_int8", "pa_decode_order", "pa_copy_blocks", "pa_gather_kv",
+               "pa_decode_static", "pa_decode_int8", "pa_decode_order", "pa_copy_blocks", "pa_gather_kv",
                "pa_validate_prefill_metadata", "pa_validate_decode_metadata"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
@@ -286,6 +287,32 @@ def pa_decode(q, k_pool, v_pool, context_lens, block_table, max_context_len, sof
         _ptr(q), _row_stride(q, hq * d, "q"), hq, _ptr(k_pool), _ptr(v_pool), ctypes.byref(pool),
         _ptr(context_lens), _ptr(block_table), block_table.shape[1], b, int(max_context_len),
         float(softmax_scale), _ptr(row_order), _ptr(out), _ptr(workspace), wbytes, _stream()))
+    return out
+
+
+def pa_decode_static(q, k_pool, v_pool, context_lens, block_table, max_context_len, softmax_scale,
+                     out=None, row_order=None):
+    """pa_decode with its split partials in the library's per-GPU scratch
+    array instead of a workspace (no allocation by the call)."""
+    lib = load()
+    _dev(q, k_pool, v_pool)
+    pool = pool_desc(k_pool)
+    b, hq, d = q.shape
+    if d != pool.head_dim or q.dtype != k_pool.dtype:
+        raise ValueError("q must match the pools' head_dim and dtype")
+    context_lens, block_table = _i32(context_lens, "context_lens"), _i32(block_table, "block_table")
+    if row_order is not None:
+        row_order = _i32(row_order, "row_order")
+        if row_order.numel() != b:
+            raise ValueError("row_order must hold one entry per sequence")
+    if out is None:
+        out = torch.empty((b, hq, d), dtype=q.dtype, device=q.device)
+    elif not out.is_contiguous() or out.shape != (b, hq, d) or out.dtype != q.dtype:
+        raise ValueError("out must be contiguous [B, Hq, D] of q's dtype")
+    _check("pa_decode_static", lib.pa_decode_static(
+        _ptr(q), _row_stride(q, hq * d, "q"), hq, _ptr(k_pool), _ptr(v_pool), ctypes.byref(pool),
+        _ptr(context_lens), _ptr(block_table), block_table.shape[1], b, int(max_context_len),
+        float(softmax_scale), _ptr(row_order), _ptr(out), _stream()))
     return out
 
 

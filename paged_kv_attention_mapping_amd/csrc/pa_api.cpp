@@ -91,6 +91,30 @@ pa_status check_decode_int8_shape(const pa_pool *pool, int32_t num_q_heads, int3
     return PA_OK;
 }
 
+// pa_decode's host checks and split plan, shared with pa_decode_static.
+// PA_OK with num_seqs == 0 means nothing to do; *need is the partials' size.
+pa_status check_decode(const void *q, int64_t q_row_stride, int32_t num_q_heads, const void *k_pool,
+                       const void *v_pool, const pa_pool *pool, const int32_t *context_lens,
+                       const int32_t *block_table, int32_t block_table_stride, int32_t num_seqs,
+                       int32_t max_context_len, float softmax_scale, const void *out, pa::PoolGeom *g,
+                       pa::RowAttnPlan *plan, size_t *need) {
+    pa_status st = check_attention_shape(pool, num_q_heads, g);
+    if (st != PA_OK) return st;
+    if (num_seqs < 0 || max_context_len < 0) return PA_ERR_BAD_SHAPE;
+    if (!scale_ok(softmax_scale)) return PA_ERR_BAD_SHAPE;
+    if (num_seqs == 0) return PA_OK;
+    if (!q || !k_pool || !v_pool || !context_lens || !block_table || !out) return PA_ERR_NULL_ARG;
+    if (block_table_stride <= 0) return PA_ERR_BAD_SHAPE;
+    if (q_row_stride < (int64_t)num_q_heads * g->d) return PA_ERR_BAD_SHAPE;
+    const int eb = elem_bytes(g->dtype);
+    if (!aligned16(q) || (q_row_stride * eb) % 16 || !aligned16(k_pool) || !aligned16(v_pool))
+        return PA_ERR_UNSUPPORTED;
+    const int group = num_q_heads / g->hkv;
+    *plan = pa::plan_row_attention(num_seqs, *g, group, max_context_len);
+    *need = pa::row_attention_workspace_bytes(*plan, num_q_heads, g->d);
+    return PA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -240,24 +264,34 @@ pa_status pa_decode(const void *q, int64_t q_row_stride, int32_t num_q_heads, co
                     int32_t max_context_len, float softmax_scale, const int32_t *row_order, void *out,
                     void *workspace, size_t workspace_bytes, void *stream) {
     pa::PoolGeom g;
-    pa_status st = check_attention_shape(pool, num_q_heads, &g);
-    if (st != PA_OK) return st;
-    if (num_seqs < 0 || max_context_len < 0) return PA_ERR_BAD_SHAPE;
-    if (!scale_ok(softmax_scale)) return PA_ERR_BAD_SHAPE;
-    if (num_seqs == 0) return PA_OK;
-    if (!q || !k_pool || !v_pool || !context_lens || !block_table || !out) return PA_ERR_NULL_ARG;
-    if (block_table_stride <= 0) return PA_ERR_BAD_SHAPE;
-    if (q_row_stride < (int64_t)num_q_heads * g.d) return PA_ERR_BAD_SHAPE;
-    const int eb = elem_bytes(g.dtype);
-    if (!aligned16(q) || (q_row_stride * eb) % 16 || !aligned16(k_pool) || !aligned16(v_pool))
-        return PA_ERR_UNSUPPORTED;
-    const int group = num_q_heads / g.hkv;
-    const pa::RowAttnPlan plan = pa::plan_row_attention(num_seqs, g, group, max_context_len);
-    const size_t need = pa::row_attention_workspace_bytes(plan, num_q_heads, g.d);
+    pa::RowAttnPlan plan;
+    size_t need = 0;
+    pa_status st = check_decode(q, q_row_stride, num_q_heads, k_pool, v_pool, pool, context_lens, block_table,
+                                block_table_stride, num_seqs, max_context_len, softmax_scale, out, &g, &plan, &need);
+    if (st != PA_OK || num_seqs == 0) return st;
     if (need && (!workspace || workspace_bytes < need)) return PA_ERR_WORKSPACE;
     return from_hip(pa::launch_decode(q, q_row_stride, num_q_heads, k_pool, v_pool, g, context_lens,
                                       block_table, block_table_stride, plan, softmax_scale, row_order,
                                       out, workspace, (hipStream_t)stream));
+}
+
+pa_status pa_decode_static(const void *q, int64_t q_row_stride, int32_t num_q_heads, const void *k_pool,
+                           const void *v_pool, const pa_pool *pool, const int32_t *context_lens,
+                           const int32_t *block_table, int32_t block_table_stride, int32_t num_seqs,
+                           int32_t max_context_len, float softmax_scale, const int32_t *row_order, void *out,
+                           void *stream) {
+    pa::PoolGeom g;
+    pa::RowAttnPlan plan;
+    size_t need = 0;
+    pa_status st = check_decode(q, q_row_stride, num_q_heads, k_pool, v_pool, pool, context_lens, block_table,
+                                block_table_stride, num_seqs, max_context_len, softmax_scale, out, &g, &plan, &need);
+    if (st != PA_OK || num_seqs == 0) return st;
+    if (need > pa::kStaticScratchBytes) return PA_ERR_WORKSPACE;  // before any device call
+    void *ws = nullptr;
+    if (need && pa::static_scratch(&ws) != hipSuccess) return PA_ERR_HIP;
+    return from_hip(pa::launch_decode(q, q_row_stride, num_q_heads, k_pool, v_pool, g, context_lens,
+                                      block_table, block_table_stride, plan, softmax_scale, row_order,
+                                      out, ws, (hipStream_t)stream));
 }
 
 size_t pa_decode_int8_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,

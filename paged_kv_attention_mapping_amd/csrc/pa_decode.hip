@@ -30,6 +30,9 @@
 #include <type_traits>
 #include <math.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "pa_device.h"
 #include "pa_kernels.h"
 
@@ -905,6 +908,38 @@ hipError_t launch_decode_int8(const void *q, int64_t q_row_stride, int hq, int q
     if (q_dtype == 0) return dispatch_dim<float, DecodeRows, true>(g.d, group, plan.waves, a, rows, stream);
     if (q_dtype == 3) return dispatch_dim<f16_t, DecodeRows, true>(g.d, group, plan.waves, a, rows, stream);
     return dispatch_dim<bf16_t, DecodeRows, true>(g.d, group, plan.waves, a, rows, stream);
+}
+
+// pa_decode_static's scratch: the split partials of a decode call live in
+// this file-scope device array instead of a caller workspace.  In host code
+// `scratch` names a host-side stand-in, so kernels get the device address
+// that hipGetSymbolAddress returns, looked up once per device with that
+// device current and kept per device (each GPU holds its own copy).
+namespace {
+__device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+constexpr int kScratchDevices = 64;
+std::atomic<void *> g_scratch_ptr[kScratchDevices];
+std::mutex g_scratch_mu;
+}  // namespace
+
+hipError_t static_scratch(void **ptr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+    void *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess) return e;
+            if (!p) return hipErrorInvalidSymbol;
+            g_scratch_ptr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *ptr = p;
+    return hipSuccess;
 }
 
 hipError_t launch_decode_order(const int32_t *context_lens, int num_rows, int32_t *row_order,

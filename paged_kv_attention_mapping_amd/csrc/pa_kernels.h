@@ -94,6 +94,13 @@ hipError_t launch_prefill_rows_int8(const void *q, int64_t q_row_stride, int hq,
                                     int num_seqs, const RowAttnPlan &plan, float softmax_scale, void *out,
                                     void *workspace, hipStream_t stream);
 
+// The device array that pa_decode_static uses in place of a caller
+// workspace: kStaticScratchBytes per GPU, held until the process ends and
+// shared by every such call on that GPU.  static_scratch() returns its
+// address on the current device (looked up once per device).
+constexpr size_t kStaticScratchBytes = size_t(16) << 20;
+hipError_t static_scratch(void **ptr);
+
 // Longest-context-first permutation of decode rows (one workgroup).
 constexpr int kDecodeOrderMax = 2048;
 hipError_t launch_decode_order(const int32_t *context_lens, int num_rows, int32_t *row_order,

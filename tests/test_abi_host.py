@@ -28,7 +28,7 @@ def test_library_loads_and_exports_every_symbol():
     lib = pa.load()
     for name in _declared_symbols():
         assert hasattr(lib, name), name
-    assert lib.pa_abi_version() == 4
+    assert lib.pa_abi_version() == 5
     assert lib.pa_status_string(0) == b"ok"
     assert b"workspace" in lib.pa_status_string(5)
 
