@@ -210,6 +210,14 @@ def main():
     f16 = None if args.no_f16 else f16_measure(pa, W, lay, ctx_d, bt_d, order_d, dec_call_ms, pf_call_ms,
                                                max(args.steps, 2))
     c5b = None if args.no_c5b else c5b_measure(pa, W, max(args.steps, 2))
+    # the prompt's store alone (K and V rows read, then written into the pool)
+    st_ms = _time_calls([lambda: pa.pa_store_kv(pf_kn, pf_vn, pf_slots, pf_k, pf_v)], max(args.steps, 10))
+    st_bytes = 2 * 2 * pf.total_q * pf.num_kv_heads * pf.head_dim * 2
+    store = {"workload": f"pa_store_kv of {pf.total_q} tokens x {pf.num_kv_heads} KV heads x {pf.head_dim}, bf16, "
+                         f"block {pf.block_size}",
+             "avg_launch_us": round(st_ms * 1e3, 2), "bytes_per_launch": st_bytes,
+             "achieved_gbps": round(st_bytes / (st_ms * 1e-3) / 1e9, 2),
+             "frac_hbm": round(st_bytes / (st_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -277,6 +285,7 @@ def main():
         result.update(f16)
     if c5b is not None:
         result["decode_c5b"] = c5b
+    result["store"] = store
     if graph is not None:
         result["graph_step"] = graph
     result["prefill_mixed"] = mixed

@@ -4,10 +4,12 @@
 // K row and V row of token t go to flat slot slot_mapping[t] of the pools;
 // slot -1 is a padding token and is skipped.  Bits are copied unchanged.
 //
-// Design for gfx950: one lane moves one 16-byte chunk of K and one of V, so a
-// wave moves 1 KiB of each per instruction; a token row of Hkv*d elements
-// (2 KiB at 8 heads x 128 x bf16) is 128 lanes.  When the rows or the
-// pointers are not 16-byte aligned a lane copies single elements instead.
+// Design for gfx950: a wave-wide 16-byte load moves 1 KiB of K (or V); a
+// token row of Hkv*d elements (2 KiB at 8 heads x 128 x bf16) is 128 lanes.
+// A lane moves kStoreChunks such chunks of K and of V, 256 lanes apart, with
+// all of its loads issued before its first store, so each lane keeps
+// 2 * kStoreChunks * 16 bytes in flight.  When the rows or the pointers are
+// not 16-byte aligned a lane copies single elements instead.
 #include <type_traits>
 
 #include "pa_device.h"
@@ -17,22 +19,37 @@ namespace pa {
 namespace {
 
 constexpr int kStoreThreads = 256;
+constexpr int kStoreChunks = 4;  // 16-byte chunks of K (and of V) per lane
 
+// Chunk u of lane x in workgroup b is chunk (b * kStoreChunks + u) * 256 + x
+// of the flat [num_tokens][chunks_per_row] view: every load and store
+// instruction of a wave covers 1 KiB of consecutive bytes of a row.
 __global__ __launch_bounds__(kStoreThreads) void store_kv_vec16(
     const char *__restrict__ k, int64_t k_stride_bytes, const char *__restrict__ v,
     int64_t v_stride_bytes, const int32_t *__restrict__ slot_mapping, int64_t num_chunks,
     int chunks_per_row, char *__restrict__ k_pool, char *__restrict__ v_pool, int64_t num_slots) {
-    const int64_t i = (int64_t)blockIdx.x * kStoreThreads + threadIdx.x;
-    if (i >= num_chunks) return;
-    const int64_t t = i / chunks_per_row;
-    const int c = (int)(i - t * chunks_per_row);
-    const int64_t slot = slot_mapping[t];
-    if (slot < 0 || slot >= num_slots) return;  // -1: padding token
     const int64_t row_bytes = (int64_t)chunks_per_row * 16;
-    const uint4 kv = ld16(k + t * k_stride_bytes + c * 16);
-    const uint4 vv = ld16(v + t * v_stride_bytes + c * 16);
-    *reinterpret_cast<uint4 *>(k_pool + slot * row_bytes + c * 16) = kv;
-    *reinterpret_cast<uint4 *>(v_pool + slot * row_bytes + c * 16) = vv;
+    int64_t dst[kStoreChunks];
+    uint4 kv[kStoreChunks], vv[kStoreChunks];
+#pragma unroll
+    for (int u = 0; u < kStoreChunks; ++u) {
+        const int64_t i = ((int64_t)blockIdx.x * kStoreChunks + u) * kStoreThreads + threadIdx.x;
+        dst[u] = -1;
+        if (i >= num_chunks) continue;
+        const int64_t t = i / chunks_per_row;
+        const int c = (int)(i - t * chunks_per_row);
+        const int64_t slot = slot_mapping[t];
+        if (slot < 0 || slot >= num_slots) continue;  // -1: padding token
+        dst[u] = slot * row_bytes + c * 16;
+        kv[u] = ld16(k + t * k_stride_bytes + c * 16);
+        vv[u] = ld16(v + t * v_stride_bytes + c * 16);
+    }
+#pragma unroll
+    for (int u = 0; u < kStoreChunks; ++u) {
+        if (dst[u] < 0) continue;
+        *reinterpret_cast<uint4 *>(k_pool + dst[u]) = kv[u];
+        *reinterpret_cast<uint4 *>(v_pool + dst[u]) = vv[u];
+    }
 }
 
 template <typename W>
@@ -260,7 +277,8 @@ hipError_t launch_store_kv(const void *k, int64_t k_row_stride, const void *v, i
     if (vec) {
         const int cpr = (int)(row_bytes / 16);
         const int64_t n = (int64_t)num_tokens * cpr;
-        const unsigned grid = (unsigned)((n + kStoreThreads - 1) / kStoreThreads);
+        const int64_t per_wg = (int64_t)kStoreThreads * kStoreChunks;
+        const unsigned grid = (unsigned)((n + per_wg - 1) / per_wg);
         hipLaunchKernelGGL(store_kv_vec16, dim3(grid), dim3(kStoreThreads), 0, stream,
                            (const char *)k, k_row_stride * eb, (const char *)v, v_row_stride * eb,
                            slot_mapping, n, cpr, (char *)k_pool, (char *)v_pool, num_slots);
