@@ -217,7 +217,8 @@ def main():
                          f"block {pf.block_size}",
              "avg_launch_us": round(st_ms * 1e3, 2), "bytes_per_launch": st_bytes,
              "achieved_gbps": round(st_bytes / (st_ms * 1e-3) / 1e9, 2),
-             "frac_hbm": round(st_bytes / (st_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+             "frac_hbm": round(st_bytes / (st_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+             "traffic": measured_traffic("store")}
 
     cpu = None
     if not args.no_cpu_baseline:
