@@ -39,7 +39,9 @@
  * type of the fork's fused-dequantization microbenchmark: LLM inference
  * interview notes (nano-vllm fork), Q3, the INT8-versus-FP16 latency table);
  * head_dim 32, 64, 128 or 256;
- * block_size a power of two (1 .. 65536); num_q_heads a multiple of
+ * block_size a power of two (1 .. 65536); num_kv_heads at most 65536, with
+ * num_kv_heads * block_size below 2^31 (PA_ERR_UNSUPPORTED otherwise: the
+ * kernels index a block's (slot, head) rows in 32 bits); num_q_heads a multiple of
  * num_kv_heads with group size num_q_heads / num_kv_heads in {1, 2, 4, 8}.
  * Query head h reads KV head h / (num_q_heads / num_kv_heads).
  * The bf16 and fp16 prefills run on MFMA for head_dim 64 and 128; every
@@ -56,7 +58,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 5
+#define PA_ABI_VERSION 6
 
 typedef enum {
     PA_OK = 0,

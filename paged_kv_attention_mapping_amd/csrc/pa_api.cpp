@@ -36,6 +36,9 @@ pa_status check_pool(const pa_pool *pool, pa::PoolGeom *g) {
     if (pool->num_blocks < 0 || pool->block_size <= 0 || pool->num_kv_heads <= 0 || pool->head_dim <= 0)
         return PA_ERR_BAD_SHAPE;
     if (!is_pow2(pool->block_size) || pool->block_size > 65536) return PA_ERR_UNSUPPORTED;
+    // a block's (slot, head) rows are indexed in 32 bits, offset * heads in 24
+    if (pool->num_kv_heads > 65536 || (int64_t)pool->num_kv_heads * pool->block_size >= (int64_t(1) << 31))
+        return PA_ERR_UNSUPPORTED;
     g->num_blocks = pool->num_blocks;
     g->block_size = pool->block_size;
     g->block_shift = log2i(pool->block_size);

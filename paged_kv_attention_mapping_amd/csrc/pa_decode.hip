@@ -164,6 +164,18 @@ __device__ __forceinline__ int split_tokens_of(int ctx, int num_splits, int roun
     return min(max(st, round_tokens), split_cap);
 }
 
+// Index of the (slot, KV head) row that offset `off` of physical block `blk`
+// holds for KV head `head` in a [num_blocks][block_size][hkv][...] pool: one
+// 32 x 32 -> 64-bit multiply-add (the pool checks keep blk_rows = hkv *
+// block_size below 2^31 and hkv at most 65536, so off * hkv fits 24-bit
+// operands).  A masked token (blk < 0) maps to row `head` of slot 0: every
+// such load hits one cached line.
+__device__ __forceinline__ uint64_t kv_row_index(int blk, int off, uint32_t blk_rows, int hkv, int head) {
+    const bool ok = blk >= 0;
+    const uint32_t r = (ok ? __umul24((uint32_t)off, (uint32_t)hkv) : 0u) + (uint32_t)head;
+    return (uint64_t)(ok ? (uint32_t)blk : 0u) * blk_rows + r;
+}
+
 // This lane's slice of one query head, kept in the form the dot product wants:
 // bf16 and fp16 stay packed (two elements per 32-bit word, consumed by
 // v_dot2_f32_bf16 / v_dot2_f32_f16); fp32 is kept as floats.
@@ -269,8 +281,7 @@ __global__ __launch_bounds__(NW * kWave) void row_attn_split(RowArgs a, Rows row
 
     const T *kp = reinterpret_cast<const T *>(a.k_pool);
     const T *vp = reinterpret_cast<const T *>(a.v_pool);
-    const int64_t head_off = (int64_t)g * D + c * EPV;
-    const int64_t slot_stride = (int64_t)hkv * D;
+    const uint32_t blk_rows = (uint32_t)hkv << a.block_shift;
 
     float m[G], l[G], acc[G][EPV];
 #pragma unroll
@@ -294,9 +305,9 @@ __global__ __launch_bounds__(NW * kWave) void row_attn_split(RowArgs a, Rows row
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
             const int tok = base + (u * kNW + w) * TPW + tg;
-            const int64_t slot = blk[u] >= 0 ? ((int64_t)blk[u] << shift) + (tok & bmask) : 0;
-            kr[u] = ld16_stream(kp + slot * slot_stride + head_off);
-            vr[u] = ld16_stream(vp + slot * slot_stride + head_off);
+            const uint64_t e = kv_row_index(blk[u], tok & bmask, blk_rows, hkv, g) * D + c * EPV;
+            kr[u] = ld16_stream(kp + e);
+            vr[u] = ld16_stream(vp + e);
         }
     };
     auto consume = [&](const uint4 (&kr)[kUnroll], const uint4 (&vr)[kUnroll], const int (&blk)[kUnroll]) {
@@ -314,12 +325,12 @@ __global__ __launch_bounds__(NW * kWave) void row_attn_split(RowArgs a, Rows row
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u) mx = fmaxf(mx, sc[u][j]);
             const float m_use = (mx == -INFINITY) ? 0.f : mx;
-            const float alpha = exp2f(m[j] - m_use);
+            const float alpha = __builtin_amdgcn_exp2f(m[j] - m_use);
             m[j] = mx;
             float ps = 0.f;
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u) {
-                sc[u][j] = exp2f(sc[u][j] - m_use);
+                sc[u][j] = __builtin_amdgcn_exp2f(sc[u][j] - m_use);
                 ps += sc[u][j];
             }
             l[j] = l[j] * alpha + ps;
@@ -416,8 +427,19 @@ __global__ __launch_bounds__(NW * kWave) void row_attn_split(RowArgs a, Rows row
 // pair (1024 + u0, 1024 + u1), exact integers, and v_dot2_f32_f16 takes them
 // against the queries in fp16 (exact for bf16 values inside fp16's range);
 // the dot is sum q (1152 + code) - 1152 sum q.  fp32 queries use fp32
-// products of the widened u.  V: u widened to fp32, and the
-// accumulator subtracts 128 * sum of the folded p at the end.
+// products of the widened u.  V, with bf16 or fp16 queries: the lane's two
+// tokens of a round meet in v_dot2_f32_f16, the folded p of both rounded to
+// an fp16 pair, against each element's two codes as the fp16 pair (1024 +
+// u_t0, 1024 + u_t1) (one byte permute and one XOR): half the instructions of
+// widening the codes and accumulating in fp32.  The accumulator then holds
+// sum p' (1152 + code) and subtracts 1152 * sum p' over the same rounded p'.
+// fp32 queries keep fp32 products of the widened u and subtract 128 * sum p.
+//
+// Workgroup order: the virtual heads of one (row, split) are dealt to
+// workgroups 8 apart, which the dispatcher places on one XCD (workgroups go
+// round-robin over the 8 XCDs): a token's scales, one 16-byte run for all its
+// KV heads, are then fetched from HBM once, into that XCD's L2, rather than
+// once per head.  The grid is padded to whole groups of 8 (row, split) units.
 template <typename TQ, int D, int G, int NW, class Rows>
 __global__ __launch_bounds__(NW * kWave) void row_attn_int8(RowArgs a, Rows rows) {
     constexpr int EPV = 16, LPT = D / EPV, TPW = kWave / LPT, TPR = NW * TPW * kUnroll;
@@ -437,10 +459,11 @@ __global__ __launch_bounds__(NW * kWave) void row_attn_int8(RowArgs a, Rows rows
     const int hkv = a.hkv, hq = hkv * G;
     const int hkv_p = hkv >> a.kv_shift;
 
-    const int64_t wg = blockIdx.x;
-    const int g = (int)(wg % hkv);
+    const int64_t r8 = (int64_t)blockIdx.x >> 3;
+    const int g = (int)(r8 % hkv);
     const int gp = g >> a.kv_shift;
-    const int64_t rest = wg / hkv;
+    const int64_t rest = (blockIdx.x & 7) + 8 * (r8 / hkv);
+    if (rest >= (int64_t)a.num_rows * a.num_splits) return;  // grid padding
     const int split = (int)(rest % a.num_splits);
     const int row = rows.row_of((int)(rest / a.num_splits));
     int seq, ctx;
@@ -500,15 +523,17 @@ __global__ __launch_bounds__(NW * kWave) void row_attn_int8(RowArgs a, Rows rows
 
     const int8_t *kp = reinterpret_cast<const int8_t *>(a.k_pool);
     const int8_t *vp = reinterpret_cast<const int8_t *>(a.v_pool);
-    const int64_t head_off = (int64_t)gp * D + c * EPV;
-    const int64_t slot_stride = (int64_t)hkv_p * D;
+    const uint32_t blk_rows = (uint32_t)hkv_p << a.block_shift;
 
-    float m[G], l[G], ps[G], acc[G][EPV];
+    // ps: sum of the folded p (fp32 V path); vsum: sum of the same p rounded
+    // to fp16 (fp16 V pairs)
+    float m[G], l[G], ps[G], vsum[G], acc[G][EPV];
 #pragma unroll
     for (int j = 0; j < G; ++j) {
         m[j] = -INFINITY;
         l[j] = 0.f;
         ps[j] = 0.f;
+        vsum[j] = 0.f;
 #pragma unroll
         for (int e = 0; e < EPV; ++e) acc[j][e] = 0.f;
     }
@@ -531,11 +556,11 @@ __global__ __launch_bounds__(NW * kWave) void row_attn_int8(RowArgs a, Rows rows
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
             const int tok = base + (u * NW + w) * TPW + tg;
-            const int64_t slot = blk[u] >= 0 ? ((int64_t)blk[u] << shift) + (tok & bmask) : 0;
-            kr[u] = ld16_stream(kp + slot * slot_stride + head_off);
-            vr[u] = ld16_stream(vp + slot * slot_stride + head_off);
-            ks[u] = (float)a.k_scale[slot * hkv_p + gp];
-            vs[u] = (float)a.v_scale[slot * hkv_p + gp];
+            const uint64_t ri = kv_row_index(blk[u], tok & bmask, blk_rows, hkv_p, gp);
+            kr[u] = ld16_stream(kp + ri * D + c * EPV);
+            vr[u] = ld16_stream(vp + ri * D + c * EPV);
+            ks[u] = (float)a.k_scale[ri];
+            vs[u] = (float)a.v_scale[ri];
         }
     };
     auto consume = [&](const uint4 (&kr)[kUnroll], const uint4 (&vr)[kUnroll], const float (&ks)[kUnroll],
@@ -580,32 +605,61 @@ __global__ __launch_bounds__(NW * kWave) void row_attn_int8(RowArgs a, Rows rows
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u) mx = fmaxf(mx, sc[u][j]);
             const float m_use = (mx == -INFINITY) ? 0.f : mx;
-            const float alpha = exp2f(m[j] - m_use);
+            const float alpha = __builtin_amdgcn_exp2f(m[j] - m_use);
             m[j] = mx;
             float pl = 0.f, pv = 0.f;
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u) {
-                const float p = exp2f(sc[u][j] - m_use);
+                const float p = __builtin_amdgcn_exp2f(sc[u][j] - m_use);
                 pl += p;
                 sc[u][j] = blk[u] >= 0 ? p * vs[u] : 0.f;  // V scale folded into p
                 pv += sc[u][j];
             }
             l[j] = l[j] * alpha + pl;
             ps[j] = ps[j] * alpha + pv;
+            vsum[j] *= alpha;
             // rescale only if the max moved for some lane of the wave (after the
             // first rounds it seldom does; a skipped rescale is by alpha = 1)
             if (__builtin_amdgcn_ballot_w64(alpha != 1.f))
 #pragma unroll
             for (int e = 0; e < EPV; ++e) acc[j][e] *= alpha;
         }
+        if constexpr (kF16Dot) {
+            static_assert(kUnroll % 2 == 0, "tokens of a round pair up");
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            float vu[EPV];
-            widen(vr[u], vu);
+            for (int u = 0; u < kUnroll; u += 2) {
+                half2_t pp[G];
 #pragma unroll
-            for (int j = 0; j < G; ++j)
+                for (int j = 0; j < G; ++j) {
+                    const _Float16 p0 = (_Float16)sc[u][j], p1 = (_Float16)sc[u + 1][j];
+                    pp[j] = (half2_t){p0, p1};
+                    vsum[j] += (float)p0 + (float)p1;
+                }
+                const uint32_t c0[4] = {vr[u].x, vr[u].y, vr[u].z, vr[u].w};
+                const uint32_t c1[4] = {vr[u + 1].x, vr[u + 1].y, vr[u + 1].z, vr[u + 1].w};
 #pragma unroll
-                for (int e = 0; e < EPV; ++e) acc[j][e] = fmaf(sc[u][j], vu[e], acc[j][e]);
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int b = 0; b < 4; ++b) {
+                        // byte b of each token's word i into the low bytes of the two
+                        // halves (zeros above), then sign flip and fp16 exponent at once
+                        const uint32_t pair = __builtin_amdgcn_perm(c1[i], c0[i], 0x0c040c00u + 0x00010001u * b);
+                        const half2_t vv = __builtin_bit_cast(half2_t, pair ^ 0x64806480u);
+#pragma unroll
+                        for (int j = 0; j < G; ++j)
+                            acc[j][4 * i + b] = __builtin_amdgcn_fdot2(pp[j], vv, acc[j][4 * i + b], false);
+                    }
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                float vu[EPV];
+                widen(vr[u], vu);
+#pragma unroll
+                for (int j = 0; j < G; ++j)
+#pragma unroll
+                    for (int e = 0; e < EPV; ++e) acc[j][e] = fmaf(sc[u][j], vu[e], acc[j][e]);
+            }
         }
     };
     {
@@ -621,11 +675,15 @@ __global__ __launch_bounds__(NW * kWave) void row_attn_int8(RowArgs a, Rows rows
             consume(kB, vB, ksB, vsB, bB);
         }
     }
-    // codes were offset by 128: remove 128 * (sum of folded p) from every element
+    // codes were offset by 1152 (fp16 pairs) or 128 (fp32): remove that times
+    // the sum of the folded p from every element
 #pragma unroll
     for (int j = 0; j < G; ++j)
 #pragma unroll
-        for (int e = 0; e < EPV; ++e) acc[j][e] = fmaf(-128.f, ps[j], acc[j][e]);
+        for (int e = 0; e < EPV; ++e) {
+            if constexpr (kF16Dot) acc[j][e] = fmaf(-1152.f, vsum[j], acc[j][e]);
+            else acc[j][e] = fmaf(-128.f, ps[j], acc[j][e]);
+        }
 
     // ---- combine the token groups of the wave, then the waves (as row_attn_split)
 #pragma unroll
@@ -753,8 +811,9 @@ int tokens_per_round(int dtype, int d, int nw) {
 
 template <typename T, int D, int G, int NW, class Rows, bool I8 = false>
 hipError_t run_rows(const RowArgs &a, const Rows &rows, hipStream_t stream) {
-    const int64_t wgs = (int64_t)a.num_rows * a.num_splits * a.hkv;
+    int64_t wgs = (int64_t)a.num_rows * a.num_splits * a.hkv;
     if (wgs == 0) return hipSuccess;
+    if constexpr (I8) wgs = ((int64_t)a.num_rows * a.num_splits + 7) / 8 * 8 * a.hkv;  // whole groups of 8 units
     if constexpr (I8)
         hipLaunchKernelGGL((row_attn_int8<T, D, G, NW, Rows>), dim3((unsigned)wgs), dim3(NW * kWave), 0,
                            stream, a, rows);

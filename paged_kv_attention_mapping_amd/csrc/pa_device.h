@@ -73,9 +73,11 @@ template <> __device__ __forceinline__ void store_elem<f16_t>(f16_t *p, float x)
 // row_half_mirror = 0x141, row_mirror = 0x140.  After the steps up to N every
 // lane of an aligned group of N lanes holds the same (commutative) sum.
 
+// Every lane of a row is a valid source for these controls, so bound_ctrl
+// never applies; with it set (and no old value) the compiler folds the move
+// into the consuming add or max (v_add_f32_dpp), one instruction per step.
 template <int CTRL> __device__ __forceinline__ float dpp_f(float x) {
-    int xi = __float_as_int(x);
-    return __int_as_float(__builtin_amdgcn_update_dpp(xi, xi, CTRL, 0xF, 0xF, false));
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
 }
 
 template <int N> __device__ __forceinline__ float group_sum(float x) {

@@ -28,7 +28,7 @@ def test_library_loads_and_exports_every_symbol():
     lib = pa.load()
     for name in _declared_symbols():
         assert hasattr(lib, name), name
-    assert lib.pa_abi_version() == 5
+    assert lib.pa_abi_version() == 6
     assert lib.pa_status_string(0) == b"ok"
     assert b"workspace" in lib.pa_status_string(5)
 
@@ -168,6 +168,14 @@ def test_host_argument_errors_return_before_launch():
     # block size must be a power of two
     odd = _pool(bs=12)
     assert lib.pa_store_kv(None, 64, None, 64, None, 0, None, None, ctypes.byref(odd), None) == 4
+    # at most 65536 KV heads, and fewer than 2^31 (slot, head) rows per block
+    for hkv, bs in ((65537, 1), (32768, 65536), (65536, 32768)):
+        big = _pool(hkv=hkv, bs=bs)
+        assert lib.pa_store_kv(None, 64, None, 64, None, 0, None, None, ctypes.byref(big), None) == 4, (hkv, bs)
+        assert lib.pa_decode(None, 64, hkv, None, None, ctypes.byref(big), None, None, 1, 3, 10, 0.1,
+                             None, None, None, 0, None) == 4, (hkv, bs)
+    ok = _pool(hkv=65536, bs=16384)  # 2^30 rows per block: allowed
+    assert lib.pa_store_kv(None, 64, None, 64, None, 0, None, None, ctypes.byref(ok), None) == 0
     # group size 3 is not built; head_dim 48 is not built
     args = [None, 96, 6, None, None, None, None, None, None, None, 1, 1, 1, 1, 1, 0.1, None, None, 0, None]
     args[5] = ctypes.byref(_pool(hkv=2))
