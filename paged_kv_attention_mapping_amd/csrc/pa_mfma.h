@@ -81,11 +81,15 @@ __device__ __forceinline__ int swap_bits_2_3(int i) {
 }
 
 // 16-byte slot of logical chunk c in LDS row r.  K rows XOR with r: the 16
-// lanes of a K read name 16 different rows at one chunk.  V rows XOR with 4r:
-// a transpose read of 32 lanes names 4 consecutive rows x 4 adjacent chunks,
-// which 4r spreads over 16 different slots (all 64 banks).
+// lanes of a K read name 16 different rows at one chunk.  V rows XOR with 4r
+// (mod 16): a transpose read of 32 lanes names 4 consecutive rows x 4
+// adjacent chunks, which 4r spreads over 16 different slots (all 64 banks);
+// the V swizzle repeats every 4 rows, so a read 4k rows further is the same
+// lane offset plus an immediate.
 template <int CPR> __device__ __forceinline__ int k_slot(int r, int c) { return c ^ (r & (CPR - 1)); }
-template <int CPR> __device__ __forceinline__ int v_slot(int r, int c) { return c ^ ((4 * r) & (CPR - 1)); }
+template <int CPR> __device__ __forceinline__ int v_slot(int r, int c) {
+    return c ^ ((4 * r) & (CPR < 16 ? CPR - 1 : 15));
+}
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));

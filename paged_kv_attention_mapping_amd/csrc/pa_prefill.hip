@@ -118,7 +118,11 @@ struct Pf {
                   "int8 row split");
     static_assert(NW != 8 || 4 * MERGE * 64 * 4 <= 2 * STEPB + 2 * STAGEB, "merge area fits in the INT8 layout");
     static_assert(LPW * RPI == kRowsPerWave && LPW >= 1, "row split");
-    static_assert((4 * RPI) % CPR == 0, "V swizzle independent of the load index");
+    // V rows swizzle by 4r mod min(CPR, 16): the same for every wave-wide load
+    // when 4*RPI is a multiple of that (d <= 128), else each load has its own
+    // lane offset
+    static constexpr int VOFFS = (4 * RPI) % (CPR < 16 ? CPR : 16) == 0 ? 1 : LPW;
+    static_assert(D <= 128 || NW == 4, "head_dim 256: the 4-wave layout only (its LDS)");
     static_assert(NW != 8 || 4 * MERGE * 64 * 4 <= 4 * STEPB, "merge area fits in the K/V buffers");
 };
 
@@ -139,8 +143,8 @@ struct Pf {
 template <class C>
 __device__ __forceinline__ void load_wave_rows(const PfArgs &a, int kb_step, int kmax, int shift, int bmask,
                                                int win0, int blk0, int64_t kv_row, int64_t kv_head,
-                                               const uint32_t (&koff)[C::LPW], uint32_t voff, int w, int lane,
-                                               const int *s_blk, unsigned char *dk, unsigned char *dv) {
+                                               const uint32_t (&koff)[C::LPW], const uint32_t (&voff)[C::VOFFS], int w,
+                                               int lane, const int *s_blk, unsigned char *dk, unsigned char *dv) {
     if (kb_step + kBN * (C::KH == 2 ? w / (C::WAVES / 2) : 0) > kmax) return;
     const int row0 = __builtin_amdgcn_readfirstlane(kb_step + kRowsPerWave * w);
     if (shift >= 4 && row0 + kRowsPerWave - 1 <= kmax) {
@@ -158,7 +162,7 @@ __device__ __forceinline__ void load_wave_rows(const PfArgs &a, int kb_step, int
             for (int u = 0; u < C::LPW; ++u) {
                 const int soff = __builtin_amdgcn_readfirstlane(u * C::RPI * row_bytes);
                 buffer_lds16(rk, koff[u], soff, lk + u * 1024);
-                buffer_lds16(rv, voff, soff, lv + u * 1024);
+                buffer_lds16(rv, voff[C::VOFFS == 1 ? 0 : u], soff, lv + u * 1024);
             }
             return;
         }
@@ -482,6 +486,66 @@ __device__ __forceinline__ void attend_tile(const unsigned char *kbuf, const uns
         st_.o[k % C::DT] = C::M::mfma(va1[k], k < C::DT ? p1_lo : p1_hi, st_.o[k % C::DT]);
 }
 
+// The same tile for head_dim 256 (KS = 16 k-steps, DT = 8 output blocks):
+// the K operands of the two 32-key blocks (64 registers each) and the V^T
+// operands of a block (64) are not all held at once; each block's operands
+// are read just before its MFMAs, which leaves room for the wave's 128
+// output accumulators and 64 query registers.
+template <class C>
+__device__ __forceinline__ void attend_tile_wide(const unsigned char *kbuf, const unsigned char *vbuf,
+                                                 const int (&kofs)[C::KS], const int (&vofs)[C::DT],
+                                                 const typename C::x8 (&qf)[C::KS], SoftState<C> &st_, bool need_mask,
+                                                 int thr, float c) {
+    constexpr int NPV = 2 * C::DT;
+    const f32x16 zero = {};
+    f32x16 sacc[2];
+    typename C::x8 p_lo[2], p_hi[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        sacc[t] = zero;
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks) {
+            const typename C::x8 ka = *reinterpret_cast<const typename C::x8 *>(kbuf + kofs[ks] + t * 32 * C::ROWB);
+            sacc[t] = C::M::mfma(ka, qf[ks], sacc[t]);
+        }
+        if (need_mask) mask_block(sacc[t], t, thr);
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        f32x16 pf;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) probs_step(sacc[t], c, st_.mc, i, pf);
+        float ls = probs_finish<C>(pf, p_lo[t], p_hi[t]);
+        const bool big = __any(!(ls <= C::M::kBlockSumMax));
+        if (__builtin_expect((!st_.m_set) | big, 0)) {
+            if (t == 1) {  // block 0's products use the reference block 1 moves: finish them first
+#pragma unroll
+                for (int k = 0; k < NPV; ++k)
+                    st_.o[k % C::DT] = C::M::mfma(read_vt<C>(vbuf, vofs, k / C::DT, k % C::DT),
+                                                  k < C::DT ? p_lo[0] : p_hi[0], st_.o[k % C::DT]);
+            }
+            ls = rebase_block<C>(sacc[t], st_.o, st_.m, st_.l, c, p_lo[t], p_hi[t]);
+            st_.m_set = true;
+            st_.mc = (st_.m == -INFINITY) ? 0.f : st_.m * c;
+            if (t == 1) {
+                st_.l += ls;
+#pragma unroll
+                for (int k = 0; k < NPV; ++k)
+                    st_.o[k % C::DT] = C::M::mfma(read_vt<C>(vbuf, vofs, 2 + k / C::DT, k % C::DT),
+                                                  k < C::DT ? p_lo[1] : p_hi[1], st_.o[k % C::DT]);
+                return;
+            }
+        }
+        st_.l += ls;
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int k = 0; k < NPV; ++k)
+            st_.o[k % C::DT] = C::M::mfma(read_vt<C>(vbuf, vofs, 2 * t + k / C::DT, k % C::DT),
+                                          k < C::DT ? p_lo[t] : p_hi[t], st_.o[k % C::DT]);
+}
+
 // One step of a wave: the direct loads of the next step into (nk, nv), if
 // `load`, then the wave's tile of this step from cur, if `tile`.  The three
 // step buffers are distinct (restrict), which tells the compiler that the
@@ -491,18 +555,22 @@ __device__ __forceinline__ void attend_tile(const unsigned char *kbuf, const uns
 template <class C>
 __device__ __forceinline__ void load_and_attend(const PfArgs &a, bool load, int kb1, int kmax, int shift, int bmask,
                                                 int win0, int blk0, int64_t kv_row, int64_t kv_head,
-                                                const uint32_t (&koff)[C::LPW], uint32_t voff, int w, int lane,
+                                                const uint32_t (&koff)[C::LPW], const uint32_t (&voff)[C::VOFFS],
+                                                int w, int lane,
                                                 const int *s_blk, unsigned char *__restrict__ nk,
                                                 unsigned char *__restrict__ nv, bool tile,
                                                 const unsigned char *__restrict__ cur, const int (&kofs)[C::KS],
                                                 const int (&vofs)[C::DT], const typename C::x8 (&qf)[C::KS],
                                                 SoftState<C> &st, bool need_mask, int thr, float c) {
     if (load) load_wave_rows<C>(a, kb1, kmax, shift, bmask, win0, blk0, kv_row, kv_head, koff, voff, w, lane, s_blk, nk, nv);
-    if (tile) attend_tile<C>(cur, cur, kofs, vofs, qf, st, need_mask, thr, c);
+    if (tile) {
+        if constexpr (C::KS > 8) attend_tile_wide<C>(cur, cur, kofs, vofs, qf, st, need_mask, thr, c);
+        else attend_tile<C>(cur, cur, kofs, vofs, qf, st, need_mask, thr, c);
+    }
 }
 
 template <int D, int NH, bool I8, typename E, int NW>
-__global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void prefill_mfma_kernel(PfArgs a) {
+__global__ __launch_bounds__(64 * NW, (NW == 8 || D > 128) ? 1 : 2) void prefill_mfma_kernel(PfArgs a) {
     using C = Pf<D, NH, E, NW>;
     constexpr int kStep = C::STEP;
     constexpr int kPfThreads = C::THREADS;
@@ -586,11 +654,15 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void prefill_mfma_kernel(
     // (the row RPI*u itself is a scalar offset; the V swizzle is the same for
     // every u because 4*RPI is a multiple of CPR)
     uint32_t koff[C::LPW];
-    const uint32_t voff = (uint32_t)((lane / C::CPR) * kv_row * 2 + v_slot<C::CPR>(lane / C::CPR, lane % C::CPR) * 16);
+    uint32_t voff[C::VOFFS];
 #pragma unroll
-    for (int u = 0; u < C::LPW; ++u)
+    for (int u = 0; u < C::VOFFS; ++u)
+        voff[u] = (uint32_t)((lane / C::CPR) * kv_row * 2 +
+                             v_slot<C::CPR>(C::RPI * u + lane / C::CPR, lane % C::CPR) * 16);
+#pragma unroll
+    for (int u = 0; u < C::LPW; ++u)  // (the wave's first row, 16w, matters for the K swizzle when CPR = 32)
         koff[u] = (uint32_t)((lane / C::CPR) * kv_row * 2 +
-                             k_slot<C::CPR>(C::RPI * u + lane / C::CPR, lane % C::CPR) * 16);
+                             k_slot<C::CPR>(kRowsPerWave * w + C::RPI * u + lane / C::CPR, lane % C::CPR) * 16);
     float *merge = reinterpret_cast<float *>(s_mem) + wl * (C::MERGE * 64);
 
     for (int it = 0; it < 2; ++it) {
@@ -829,7 +901,7 @@ void plan_prefill(PfArgs &a, int num_seqs, int max_seqlen_q, bool &w4) {
 bool prefill_mfma_supported(const PoolGeom &g, int group) {
     // 16 pool rows (one wave's share of a step) must span < 2^31 bytes for
     // the 32-bit buffer offsets
-    return (g.dtype == 1 || g.dtype == 3) && (g.d == 64 || g.d == 128) && g.block_size >= 4 &&
+    return (g.dtype == 1 || g.dtype == 3) && (g.d == 64 || g.d == 128 || g.d == 256) && g.block_size >= 4 &&
            (group == 1 || group == 2 || group == 4 || group == 8) &&
            (int64_t)g.hkv * g.d * 2 * kRowsPerWave < ((int64_t)1 << 31);
 }
@@ -859,6 +931,11 @@ hipError_t launch_prefill_mfma(const void *q, int64_t q_row_stride, int hq, cons
     if (max_seqlen_q <= 0) return hipSuccess;
     bool w4;
     plan_prefill(a, num_seqs, max_seqlen_q, w4);
+    if (g.d == 256) {  // 4-wave layout only: its 64-key steps of 512-byte rows fill 128 KB of LDS
+        a.single = 1;
+        return g.dtype == 3 ? dispatch_nh<256, false, f16_t, 4>(a, num_seqs, max_seqlen_q, stream)
+                            : dispatch_nh<256, false, bf16_t, 4>(a, num_seqs, max_seqlen_q, stream);
+    }
     if (g.dtype == 3)
         return g.d == 128 ? (w4 ? dispatch_nh<128, false, f16_t, 4>(a, num_seqs, max_seqlen_q, stream)
                                 : dispatch_nh<128, false, f16_t, 8>(a, num_seqs, max_seqlen_q, stream))

@@ -107,6 +107,24 @@ def test_ragged_shapes_and_offsets(dtype, d, hq, hkv, bs):
     assert max_abs_err(got, ref) <= tol(dtype)
 
 
+@pytest.mark.parametrize("dtype,hq,hkv,bs,q_lens,q_offs", [
+    ("bf16", 8, 8, 4, [700, 33, 1, 0, 257], [0, 100, 7, 3, 1000]),   # group 1, smallest MFMA block
+    ("bf16", 16, 4, 256, [1500, 64], [37, 0]),                        # group 4, block 256
+    ("f16", 8, 4, 16, [2048], [0]),                                   # group 2: a long prompt, every row
+    ("bf16", 16, 2, 32, [300, 5, 129], [0, 600, 31]),                 # group 8
+])
+def test_head_dim_256_on_the_matrix_cores(dtype, hq, hkv, bs, q_lens, q_offs):
+    """head_dim 256 prefill (4-wave layout, operands read per 32-key block):
+    many key steps, ragged tails, cached prefixes, every row against the
+    oracle."""
+    case = W.make_prefill("d256", 9700 + hq + bs, q_lens, q_offs, hq, hkv, 256, bs, dtype)
+    say(f"[prefill] d=256 {dtype} {hq}/{hkv} bs={bs} q={q_lens}")
+    got, ref, _ = run_prefill(case)
+    err = max_abs_err(got, ref)
+    say(f"  max-abs {err:.3e}")
+    assert err <= tol(dtype)
+
+
 def test_single_visible_key_rows_return_v():
     """Row 0 of a fresh prompt sees key 0 only: the output is V[0] (to bf16 rounding)."""
     case = W.make_prefill("one", 8, [1, 64, 129], [0, 0, 0], 16, 8, 128, 16, "bf16")
