@@ -205,6 +205,7 @@ def main():
 
     graph = None if args.no_graph else graph_measure(step, ms_per_step, max(args.steps, 2))
     mixed = mixed_prefill_measure(pa, W, max(args.steps, 2))
+    d256 = d256_prefill_measure(pa, W, max(args.steps, 2))
     small = None if args.no_small else small_configs_measure(pa, W)
 
     f16 = None if args.no_f16 else f16_measure(pa, W, lay, ctx_d, bt_d, order_d, dec_call_ms, pf_call_ms,
@@ -245,6 +246,7 @@ def main():
                                 "q": 5332},
             "prefill_mixed_8192": {"lengths_table": W.c5a_mixed(with_values=False).seed, "k_pool": 5400,
                                    "v_pool": 5401, "q": 5402},
+            "prefill_d256_1x4096": {"lengths_table": 5500, "k_pool": 5501, "v_pool": 5502, "q": 5503},
         },
         "config": {
             "workload": (f"qwen3-0.6b attention step: store+prefill 1x4096 causal (block 16) + "
@@ -290,6 +292,7 @@ def main():
     if graph is not None:
         result["graph_step"] = graph
     result["prefill_mixed"] = mixed
+    result["prefill_d256"] = d256
     if small is not None:
         result["small_configs"] = small
     print(json.dumps(result), flush=True)
@@ -442,6 +445,30 @@ def mixed_prefill_measure(pa, W, reps):
             "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
                          "traffic": measured_traffic("prefill_mixed")}}
+
+
+def d256_prefill_measure(pa, W, reps):
+    """head_dim 256 on the matrix cores: one 4096-token causal prompt, 8
+    query heads over 4 KV heads, block 16, bf16 (not part of the step; the
+    Qwen3 shapes have head_dim 128)."""
+    import torch
+    dev = "cuda"
+    case = W.make_prefill("d256_1x4096", 5500, [4096], [0], 8, 4, 256, 16, "bf16", with_values=False)
+    shape = (case.num_blocks, case.block_size, case.num_kv_heads, case.head_dim)
+    kp, vp = W.device_normal(shape, 5501), W.device_normal(shape, 5502)
+    q = W.device_normal((case.total_q, case.num_q_heads, case.head_dim), 5503)
+    out = torch.empty_like(q)
+    i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)  # noqa: E731
+    args = (i32(case.cu_seqlens_q), i32(case.cu_seqlens_k), i32(case.q_offsets), i32(case.block_table))
+    ms = _time_calls([lambda: pa.pa_prefill_varlen(q, kp, vp, *args, case.max_seqlen_q, case.max_seqlen_k,
+                                                   case.scale, out=out)], reps)
+    flops = 4.0 * case.head_dim * case.num_q_heads * case.causal_pairs
+    tflops = flops / (ms * 1e-3) / 1e12
+    return {"value": round(tflops, 2), "unit": "TFLOP/s",
+            "workload": "prefill 1x4096 causal, head_dim 256, 8/4 heads, block 16, bf16",
+            "avg_launch_us": round(ms * 1e3, 2), "flops_per_launch": flops,
+            "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None}}
 
 
 def c5b_measure(pa, W, reps):

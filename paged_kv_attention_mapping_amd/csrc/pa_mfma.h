@@ -69,6 +69,7 @@ struct PfArgs {
     int num_seqs;
     int units_per_seq;      // work units (tile pairs, or single tiles) per sequence
     int single;             // 1: a unit is one query tile; 0: the pair (p, T-1-p)
+    int seq_group;          // single tiles: sequences dealt together, longest tile first (0: all of them)
     int total_q;            // rows of q and out: packed rows past it are never touched
     float scale_log2;
     uint16_t *out;

@@ -603,11 +603,22 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D > 128) ? 1 : 2) void prefill
     wg /= a.hkv;
     const int hgrp = (int)(wg % a.head_groups);
     wg /= a.head_groups;
-    // single tiles: unit u of every sequence before unit u + 1, unit u being
-    // tile T-1-u, so the longest tiles of the batch are dispatched first;
-    // pairs: sequence-major
-    const int pair = (int)(a.single ? wg / a.num_seqs : wg % a.units_per_seq);
-    const int s = (int)(a.single ? wg % a.num_seqs : wg / a.units_per_seq);
+    // single tiles: the sequences in groups of seq_group (all of them when
+    // 0), and inside a group unit u of every sequence before unit u + 1,
+    // unit u being tile T-1-u, so the group's longest tiles are dispatched
+    // first; pairs: sequence-major
+    int pair, s;
+    if (a.single) {
+        const int sg = a.seq_group > 0 ? a.seq_group : a.num_seqs;
+        const int64_t per = (int64_t)sg * a.units_per_seq;
+        const int64_t k = wg / per, loc = wg % per;
+        const int sgk = (int)min((int64_t)sg, (int64_t)a.num_seqs - k * sg);  // the last group may be short
+        pair = (int)(loc / sgk);
+        s = (int)(k * sg + loc % sgk);
+    } else {
+        pair = (int)(wg % a.units_per_seq);
+        s = (int)(wg / a.units_per_seq);
+    }
 
     // rows outside [0, total_q) are never read or written, whatever cu_seqlens_q holds
     const int q_start = min(max(a.cu_q[s], 0), a.total_q);
@@ -887,13 +898,19 @@ int64_t prefill_grid(int group, int hkv, int num_seqs, int max_seqlen_q, bool si
 //    row; with more tiles than slots, the smaller units, longest first, fill
 //    the slots more evenly (4-wave layout, measured on MI355X: 8192 new
 //    tokens over 17 sequences of 35 to 842, 56 -> 45 us against tile pairs).
-//    Sequence-major single tiles keep a sequence's tiles together in L2 and
-//    were faster for 64 equal sequences of 128 tokens (28 against 35 us) but
-//    slower for the ragged batch (49 us).
+//  * Order of single tiles: longest first across the whole batch balances a
+//    ragged batch; when every sequence has the same number of new tokens
+//    (total_q = num_seqs * max_seqlen_q, known on the host) there is nothing
+//    to balance, and groups of 4 sequences keep their K/V in L2 while their
+//    tiles run (64 sequences of 128 tokens: 39 -> 32 us).  For the ragged
+//    batch the groups cut the HBM reads from 1.29x to 1.0x the Q+K+V bytes
+//    but left long tiles of later groups to run alone at the end (52 -> 62
+//    us with groups of 8, 70 us with 4), so it keeps the batch-wide order.
 void plan_prefill(PfArgs &a, int num_seqs, int max_seqlen_q, bool &w4) {
     const bool singles_fit = prefill_grid(a.group, a.hkv, num_seqs, max_seqlen_q, true) <= kNumCUs;
     w4 = prefill_grid(a.group, a.hkv, num_seqs, max_seqlen_q, false) > kNumCUs;
     a.single = (singles_fit || w4) ? 1 : 0;
+    a.seq_group = (int64_t)a.total_q == (int64_t)num_seqs * max_seqlen_q ? 4 : 0;
 }
 
 }  // namespace

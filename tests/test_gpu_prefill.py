@@ -253,6 +253,21 @@ def test_many_short_sequences_two_workgroups_per_cu(dtype, d, hq, hkv, bs):
     assert err <= tol(dtype)
 
 
+@pytest.mark.parametrize("n,length,hq,hkv", [(67, 96, 16, 8), (64, 128, 16, 8), (9, 300, 8, 2)])
+def test_equal_length_sequences_in_groups(n, length, hq, hkv):
+    """Equal new-token counts (total_q = n * max_seqlen_q) deal single tiles
+    sequence group by sequence group (4 at a time, the last group short when
+    4 does not divide n), cached prefixes of different lengths included."""
+    rng = np.random.default_rng(7700 + n)
+    q_offs = rng.integers(0, 200, size=n, endpoint=True).tolist()
+    case = W.make_prefill("equal", 7700 + n, [length] * n, q_offs, hq, hkv, 128, 16, "bf16")
+    say(f"[prefill] {n} x {length} equal-length sequences, {hq}/{hkv}")
+    got, ref, _ = run_prefill(case)
+    err = max_abs_err(got, ref)
+    say(f"  max-abs {err:.3e}")
+    assert err <= tol("bf16")
+
+
 @pytest.mark.parametrize("q_lens,q_offs,units", [
     ([1024, 1000], [0, 37], "single tiles that exactly fill the CUs (256 workgroups, 8-wave)"),
     ([1000, 1024, 990, 1017], [0, 24, 3, 100], "tile pairs of several sequences (256 workgroups, 8-wave)"),
