@@ -211,14 +211,20 @@ def main():
     f16 = None if args.no_f16 else f16_measure(pa, W, lay, ctx_d, bt_d, order_d, dec_call_ms, pf_call_ms,
                                                max(args.steps, 2))
     c5b = None if args.no_c5b else c5b_measure(pa, W, max(args.steps, 2))
-    # the prompt's store alone (K and V rows read, then written into the pool)
-    st_ms = _time_calls([lambda: pa.pa_store_kv(pf_kn, pf_vn, pf_slots, pf_k, pf_v)], max(args.steps, 10))
+    # the prompt's store alone (K and V rows read, then written into the
+    # pool): 20 calls back to back between two events (per call: the kernel
+    # and the gap to the next), and single calls each between two events
+    # (which adds the event packets' own few microseconds to a 7 us kernel)
+    store_call = lambda: pa.pa_store_kv(pf_kn, pf_vn, pf_slots, pf_k, pf_v)  # noqa: E731
+    st_ms = _time_calls([lambda: [store_call() for _ in range(20)]], max(args.steps, 5)) / 20
+    st1_ms = _time_calls([store_call], max(args.steps, 10))
     st_bytes = 2 * 2 * pf.total_q * pf.num_kv_heads * pf.head_dim * 2
     store = {"workload": f"pa_store_kv of {pf.total_q} tokens x {pf.num_kv_heads} KV heads x {pf.head_dim}, bf16, "
                          f"block {pf.block_size}",
              "avg_launch_us": round(st_ms * 1e3, 2), "bytes_per_launch": st_bytes,
              "achieved_gbps": round(st_bytes / (st_ms * 1e-3) / 1e9, 2),
              "frac_hbm": round(st_bytes / (st_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+             "single_call_us": round(st1_ms * 1e3, 2),
              "traffic": measured_traffic("store")}
 
     cpu = None
@@ -402,9 +408,13 @@ def int8_measure(pa, W, lay, pf, k_pools, v_pools, qs, ctx_d, bt_d, order_d, pf_
     }
 
 
-def _time_calls(fns, reps):
+def _time_calls(fns, reps, queue_ahead=True):
     """Mean duration (ms) of each call in fns, from HIP events on the current
-    stream, over reps rounds after two untimed rounds."""
+    stream, over reps rounds after two untimed rounds.  With queue_ahead a
+    spin kernel of about a millisecond goes first, so the host has queued the
+    timed calls before the GPU reaches them: for calls of a few microseconds
+    the events would otherwise also time the host's launch work between them.
+    Without it (eager launch sequences), that host work is what is timed."""
     import torch
     stream = torch.cuda.current_stream()
     for _ in range(2):
@@ -413,6 +423,8 @@ def _time_calls(fns, reps):
     torch.cuda.synchronize()
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in fns]
           for _ in range(reps)]
+    if queue_ahead:
+        torch.cuda._sleep(2_000_000)
     for r in range(reps):
         for i, fn in enumerate(fns):
             ev[r][i][0].record(stream)
@@ -667,14 +679,14 @@ def f16_measure(pa, W, lay, ctx_d, bt_d, order_d, bf16_dec_ms, bf16_pf_ms, reps,
     # eager and as one captured graph
     layers28 = lambda: [pa.pa_decode(mq, mk, mv, mctx, mbt, mb.max_context_len, mb.scale, out=mout,  # noqa: E731
                                      workspace=mws) for _ in range(28)]
-    eager28 = _time_calls([layers28], max(reps, 10)) / 28
+    eager28 = _time_calls([layers28], max(reps, 10), queue_ahead=False) / 28
     layers28()
     torch.cuda.synchronize()
     g28 = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g28):
         layers28()
     torch.cuda.synchronize()
-    graph28 = _time_calls([g28.replay], max(reps, 10)) / 28
+    graph28 = _time_calls([g28.replay], max(reps, 10), queue_ahead=False) / 28
     return {
         "f16_decode": {
             "value": round(dec_gbps, 2), "unit": "GB/s",

@@ -8,7 +8,9 @@
 // token row of Hkv*d elements (2 KiB at 8 heads x 128 x bf16) is 128 lanes.
 // A lane moves kStoreChunks such chunks of K and of V, 256 lanes apart, with
 // all of its loads issued before its first store, so each lane keeps
-// 2 * kStoreChunks * 16 bytes in flight.  When the rows or the pointers are
+// 2 * kStoreChunks * 16 bytes in flight; the rows are read before (not
+// after) their slots are known, and a workgroup's row index is one scalar
+// division.  When the rows or the pointers are
 // not 16-byte aligned a lane copies single elements instead.
 #include <type_traits>
 
@@ -29,20 +31,28 @@ __global__ __launch_bounds__(kStoreThreads) void store_kv_vec16(
     int64_t v_stride_bytes, const int32_t *__restrict__ slot_mapping, int64_t num_chunks,
     int chunks_per_row, char *__restrict__ k_pool, char *__restrict__ v_pool, int64_t num_slots) {
     const int64_t row_bytes = (int64_t)chunks_per_row * 16;
+    // the workgroup's first chunk as (row, chunk) once, in scalar registers;
+    // each lane's chunks from there with 32-bit arithmetic
+    const int64_t base = (int64_t)blockIdx.x * (kStoreChunks * kStoreThreads);
+    const int64_t t_base = base / chunks_per_row;
+    const uint32_t c_base = (uint32_t)(base - t_base * chunks_per_row);
     int64_t dst[kStoreChunks];
     uint4 kv[kStoreChunks], vv[kStoreChunks];
 #pragma unroll
     for (int u = 0; u < kStoreChunks; ++u) {
-        const int64_t i = ((int64_t)blockIdx.x * kStoreChunks + u) * kStoreThreads + threadIdx.x;
+        const int64_t i = base + u * kStoreThreads + threadIdx.x;
         dst[u] = -1;
         if (i >= num_chunks) continue;
-        const int64_t t = i / chunks_per_row;
-        const int c = (int)(i - t * chunks_per_row);
-        const int64_t slot = slot_mapping[t];
-        if (slot < 0 || slot >= num_slots) continue;  // -1: padding token
-        dst[u] = slot * row_bytes + c * 16;
+        const uint32_t cu = c_base + u * kStoreThreads + threadIdx.x;  // < chunks_per_row + 1024
+        const uint32_t dt = cu / (uint32_t)chunks_per_row;
+        const int64_t t = t_base + dt;
+        const int c = (int)(cu - dt * (uint32_t)chunks_per_row);
+        // the rows are read whatever the slot holds, so their loads do not
+        // wait for the slot's
         kv[u] = ld16(k + t * k_stride_bytes + c * 16);
         vv[u] = ld16(v + t * v_stride_bytes + c * 16);
+        const int64_t slot = slot_mapping[t];
+        if (slot >= 0 && slot < num_slots) dst[u] = slot * row_bytes + c * 16;  // -1: padding token
     }
 #pragma unroll
     for (int u = 0; u < kStoreChunks; ++u) {
