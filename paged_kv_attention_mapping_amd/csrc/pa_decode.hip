@@ -559,7 +559,7 @@ __global__ __launch_bounds__(NW * kWave) void row_attn_int8(RowArgs a, Rows rows
             const uint64_t ri = kv_row_index(blk[u], tok & bmask, blk_rows, hkv_p, gp);
             kr[u] = ld16_stream(kp + ri * D + c * EPV);
             vr[u] = ld16_stream(vp + ri * D + c * EPV);
-            ks[u] = (float)a.k_scale[ri];
+            ks[u] = (float)a.k_scale[ri] * a.scale_log2;  // K scale and softmax scale, once per token
             vs[u] = (float)a.v_scale[ri];
         }
     };
@@ -584,7 +584,7 @@ __global__ __launch_bounds__(NW * kWave) void row_attn_int8(RowArgs a, Rows rows
 #pragma unroll
                     for (int i = 0; i < EPV / 2; ++i) d0 = __builtin_amdgcn_fdot2(qh[j][i], kp2[i], d0, false);
                     const float dot = group_sum<LPT>(fmaf(-1152.f, qsum[j], d0));
-                    sc[u][j] = blk[u] >= 0 ? dot * ks[u] * a.scale_log2 : -INFINITY;
+                    sc[u][j] = blk[u] >= 0 ? dot * ks[u] : -INFINITY;
                 }
             } else {
                 float ku[EPV];
@@ -595,7 +595,7 @@ __global__ __launch_bounds__(NW * kWave) void row_attn_int8(RowArgs a, Rows rows
 #pragma unroll
                     for (int e = 0; e < EPV; ++e) d0 = fmaf(qv[j][e], ku[e], d0);
                     const float dot = group_sum<LPT>(fmaf(-128.f, qsum[j], d0));
-                    sc[u][j] = blk[u] >= 0 ? dot * ks[u] * a.scale_log2 : -INFINITY;
+                    sc[u][j] = blk[u] >= 0 ? dot * ks[u] : -INFINITY;
                 }
             }
         }
@@ -633,7 +633,7 @@ __global__ __launch_bounds__(NW * kWave) void row_attn_int8(RowArgs a, Rows rows
                 for (int j = 0; j < G; ++j) {
                     const _Float16 p0 = (_Float16)sc[u][j], p1 = (_Float16)sc[u + 1][j];
                     pp[j] = (half2_t){p0, p1};
-                    vsum[j] += (float)p0 + (float)p1;
+                    vsum[j] = __builtin_amdgcn_fdot2(pp[j], (half2_t){(_Float16)1.f, (_Float16)1.f}, vsum[j], false);
                 }
                 const uint32_t c0[4] = {vr[u].x, vr[u].y, vr[u].z, vr[u].w};
                 const uint32_t c1[4] = {vr[u + 1].x, vr[u + 1].y, vr[u + 1].z, vr[u + 1].w};
