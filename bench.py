@@ -480,7 +480,8 @@ def d256_prefill_measure(pa, W, reps):
             "workload": "prefill 1x4096 causal, head_dim 256, 8/4 heads, block 16, bf16",
             "avg_launch_us": round(ms * 1e3, 2), "flops_per_launch": flops,
             "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
-                         "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None}}
+                         "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                         "traffic": measured_traffic("prefill_d256")}}
 
 
 def c5b_measure(pa, W, reps):

@@ -44,8 +44,9 @@
  * kernels index a block's (slot, head) rows in 32 bits); num_q_heads a multiple of
  * num_kv_heads with group size num_q_heads / num_kv_heads in {1, 2, 4, 8}.
  * Query head h reads KV head h / (num_q_heads / num_kv_heads).
- * The bf16 and fp16 prefills run on MFMA for head_dim 64 and 128; every
- * other supported shape runs on the vector ALU path.  Outputs of a 16-bit type are
+ * The bf16 and fp16 prefills run on MFMA for head_dim 64, 128 and 256 with
+ * block_size >= 4; every other supported shape runs on the vector ALU path.
+ * Outputs of a 16-bit type are
  * the fp32 result rounded to nearest even (fp16: beyond +-65504 it is +-inf).
  */
 #ifndef PA_H
