@@ -496,6 +496,10 @@ __global__ __launch_bounds__(NW * kWave) void row_attn_int8(RowArgs a, Rows rows
     // (bf16 and fp16 queries: as fp16 pairs for v_dot2_f32_f16, summed as fp16
     // values; exact for fp16 queries)
     constexpr bool kF16Dot = std::is_same<TQ, bf16_t>::value || std::is_same<TQ, f16_t>::value;
+    // fp16 V pairs: the folded p carry a factor 64, removed at the end (exact):
+    // p <= 1 and a scale <= 65504/127 keep p * scale * 64 below 33030, inside
+    // fp16, while small scales stay clear of fp16's subnormals 64 times longer
+    constexpr float kVsFold = kF16Dot ? 64.f : 1.f;
     typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
     float qv[G][EPV], qsum[G];
     half2_t qh[G][EPV / 2];
@@ -560,7 +564,7 @@ __global__ __launch_bounds__(NW * kWave) void row_attn_int8(RowArgs a, Rows rows
             kr[u] = ld16_stream(kp + ri * D + c * EPV);
             vr[u] = ld16_stream(vp + ri * D + c * EPV);
             ks[u] = (float)a.k_scale[ri] * a.scale_log2;  // K scale and softmax scale, once per token
-            vs[u] = (float)a.v_scale[ri];
+            vs[u] = (float)a.v_scale[ri] * kVsFold;
         }
     };
     auto consume = [&](const uint4 (&kr)[kUnroll], const uint4 (&vr)[kUnroll], const float (&ks)[kUnroll],
@@ -681,7 +685,7 @@ __global__ __launch_bounds__(NW * kWave) void row_attn_int8(RowArgs a, Rows rows
     for (int j = 0; j < G; ++j)
 #pragma unroll
         for (int e = 0; e < EPV; ++e) {
-            if constexpr (kF16Dot) acc[j][e] = fmaf(-1152.f, vsum[j], acc[j][e]);
+            if constexpr (kF16Dot) acc[j][e] = fmaf(-1152.f, vsum[j], acc[j][e]) * (1.f / kVsFold);
             else acc[j][e] = fmaf(-128.f, ps[j], acc[j][e]);
         }
 

@@ -159,6 +159,25 @@ def test_decode_int8_against_oracle(dtype, d, hq, hkv, bs, ctx):
     assert err <= tol(dtype)
 
 
+@pytest.mark.parametrize("vscale", [1e-4, 30.0])
+def test_decode_int8_v_rows_far_from_unit_size(vscale):
+    """V rows scaled by 1e-4 (fp16 scales near 3e-6) and by 30: the fp16
+    weights of the V code pairs stay accurate relative to the output's own
+    size (bf16 queries, the fp16-pair V path)."""
+    case = W.make_decode("i8_vmag", 640, [1, 300, 2048, 77, 1000], 16, 8, 128, 16, "bf16")
+    scale = lambda bits: W.f32_to_bf16_bits(W.bf16_bits_to_f32(bits) * np.float32(vscale))  # noqa: E731
+    case.v_hist, case.v_new = scale(case.v_hist), scale(case.v_new)
+    say(f"[int8 decode] V rows x {vscale}")
+    host, dev = _store_case_int8(case)
+    out = pa.pa_decode_int8(to_dev(case.q), *dev, to_dev(case.context_lens), to_dev(case.block_table),
+                            case.max_context_len, case.scale)
+    torch.cuda.synchronize()
+    ref = Q.decode(case.q, *host, case.context_lens, case.block_table, case.scale)
+    rel = max_abs_err(out, ref) / float(np.abs(ref).max())
+    say(f"  max-abs / max |ref| {rel:.3e}")
+    assert rel <= 1e-2
+
+
 def test_decode_int8_one_long_row_many_splits_and_row_order():
     """One 30000-token row (split across many workgroups and merged), plus a
     short one; the longest-first row order gives bit-identical results."""
