@@ -272,6 +272,8 @@ def main():
             "traffic": measured_traffic("decode"),
             "bytes_per_launch": kv_bytes_layer,
             "avg_launch_us": round(dec_call_ms * 1e3, 2),
+            "launch_us_median_min_max": [round(float(np.median(dec_ms)) * 1e3, 2), round(min(dec_ms) * 1e3, 2),
+                                         round(max(dec_ms) * 1e3, 2)],
             "order_us_per_step": round(float(np.mean(order_ms)) * 1e3, 2),
         },
         "prefill": {
@@ -279,6 +281,8 @@ def main():
             "unit": "TFLOP/s",
             "flops_per_launch": pf_flops,
             "avg_launch_us": round(pf_call_ms * 1e3, 2),
+            "launch_us_median_min_max": [round(float(np.median(pf_attn_ms)) * 1e3, 2),
+                                         round(min(pf_attn_ms) * 1e3, 2), round(max(pf_attn_ms) * 1e3, 2)],
             "store_plus_prefill_us": round(float(np.mean(pf_ms)) * 1e3, 2),
             "roofline": {"bound": "mfma", "achieved": round(prefill_tflops, 2),
                          "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
