@@ -303,6 +303,9 @@ def main():
         result["graph_step"] = graph
     result["prefill_mixed"] = mixed
     result["prefill_d256"] = d256
+    gemm = gemm_reference()
+    result["prefill"]["gemm_reference"] = gemm
+    result["prefill"]["frac_of_gemm_reference"] = round(prefill_tflops / gemm["tflops"], 4)
     if small is not None:
         result["small_configs"] = small
     print(json.dumps(result), flush=True)
@@ -587,6 +590,24 @@ def small_configs_measure(pa, W):
         prefill_leg(f"c2_prefill_8x{n}", W.c2_varlen(n, with_values=False), 6200 + n)
     prefill_leg("c3_prefill_2x44_after_256", W.c3_prefix(with_values=False), 6300)
     return res
+
+
+def gemm_reference(reps=10):
+    """A second denominator for the prefill: the rate of a large plain bf16
+    GEMM (8192^3, torch.mm on contiguous operands, hipBLASLt), i.e. what the
+    matrix cores sustain on this machine in a library kernel."""
+    import torch
+    n = 8192
+    g = torch.Generator(device="cuda")
+    g.manual_seed(5600)
+    a = torch.randn((n, n), generator=g, device="cuda").to(torch.bfloat16)
+    b = torch.randn((n, n), generator=g, device="cuda").to(torch.bfloat16)
+    c = torch.empty((n, n), device="cuda", dtype=torch.bfloat16)
+    ms = _time_calls([lambda: torch.mm(a, b, out=c)], reps)
+    del a, b, c
+    torch.cuda.empty_cache()
+    return {"tflops": round(2.0 * n ** 3 / (ms * 1e-3) / 1e12, 1), "shape": "8192 x 8192 x 8192 bf16, torch.mm",
+            "avg_launch_us": round(ms * 1e3, 1)}
 
 
 def graph_measure(step, eager_ms_per_step, reps):
