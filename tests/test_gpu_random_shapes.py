@@ -82,3 +82,51 @@ def test_random_decode_shapes(i):
     err = max_abs_err(out, ref)
     say(f"  max-abs {err:.3e}")
     assert err <= tol(dtype)
+
+
+INT8_CASES = 10
+
+
+@pytest.mark.parametrize("i", range(INT8_CASES))
+def test_random_int8_shapes(i):
+    """INT8 pools: the quantizing store (bit for bit against the oracle), then
+    a prefill and a decode over the same pools."""
+    from oracle import int8 as Q
+    from test_gpu_int8 import assert_pools_equal, dev_pools, int8_pools
+    rng = np.random.default_rng(9990 + i)
+    d = int(rng.choice([32, 64, 128, 256]))
+    hq, hkv = _heads(rng)
+    bs = int(rng.choice([1, 4, 16, 256]))
+    dtype = str(rng.choice(["bf16", "f16", "f32"]))
+    n = int(rng.integers(1, 9))
+    q_lens = rng.integers(1, 151, size=n).tolist()
+    q_offs = rng.integers(0, 301, size=n).tolist()
+    case = W.make_prefill("rand_i8", 9990 + i, q_lens, q_offs, hq, hkv, d, bs, dtype)
+    say(f"[random int8 {i}] {dtype} d={d} {hq}/{hkv} bs={bs} q={q_lens} off={q_offs}")
+    host = int8_pools(case.num_blocks, case.block_size, hkv, d)
+    dev = dev_pools(*host)
+    for k, v, s in ((case.k_cached, case.v_cached, case.slot_cached), (case.k_new, case.v_new, case.slot_new)):
+        if len(s):
+            pa.pa_store_kv_int8(to_dev(k), to_dev(v), to_dev(s), *dev)
+            Q.store_kv(k, v, s, *host)
+    torch.cuda.synchronize()
+    assert_pools_equal(dev, host)
+    offs = np.asarray(case.q_offsets, np.int32)
+    out = pa.pa_prefill_varlen_int8(to_dev(case.q), *dev, to_dev(case.cu_seqlens_q), to_dev(case.cu_seqlens_k),
+                                    to_dev(offs), to_dev(case.block_table), case.max_seqlen_q, case.max_seqlen_k,
+                                    case.scale)
+    torch.cuda.synchronize()
+    ref = Q.prefill(case.q, *host, case.cu_seqlens_q, case.cu_seqlens_k, offs, case.block_table, case.scale)
+    err = max_abs_err(out, ref)
+    say(f"  prefill max-abs {err:.3e}")
+    assert err <= tol(dtype)
+    # decode: the last query row of each sequence against its whole context
+    last = (np.asarray(case.cu_seqlens_q[1:]) - 1).astype(np.int64)
+    ctx = (np.asarray(case.cu_seqlens_k[1:]) - np.asarray(case.cu_seqlens_k[:-1])).astype(np.int32)
+    qd = case.q[last]
+    outd = pa.pa_decode_int8(to_dev(qd), *dev, to_dev(ctx), to_dev(case.block_table), int(ctx.max()), case.scale)
+    torch.cuda.synchronize()
+    refd = Q.decode(qd, *host, ctx, case.block_table, case.scale)
+    errd = max_abs_err(outd, refd)
+    say(f"  decode max-abs {errd:.3e}")
+    assert errd <= tol(dtype)
