@@ -10,19 +10,20 @@
 // into segments; each segment keeps its own running max m, normaliser l and
 // fp32 accumulator; a second kernel merges the segments by log-sum-exp.
 //
-// Layout on gfx950: one workgroup (4, 8 or 16 waves, chosen by the planner)
-// per (row, KV head g, split).  A
-// token's K row for head g is head_dim contiguous elements; LPT lanes each
-// load 16 bytes of it, so a wave covers 64/LPT tokens per load instruction
-// (bf16, d=128: 16 lanes x 16 B = 256 B per token, 4 tokens per wave).  The G
-// query heads that share KV head g are all served from the same K/V bytes
-// (GQA reuse, fork Q&A Q3 section 2), so every K/V byte is read from HBM once.
-// One pass: each round a lane issues all its K and V loads together (two
-// rounds in flight, 4 + 4 16-byte loads), the scores are summed across the
-// LPT lanes with DPP row operations (bf16 q.k on v_dot2_f32_bf16), and a running max,
-// normaliser and fp32 accumulator per lane group absorb the round (online
-// softmax in the log2 domain).  The groups of a wave and then the waves are
-// combined by log-sum-exp.  Block ids of a split are staged in LDS once.
+// Layout on gfx950: one workgroup (8 waves for groups of up to 2 query heads,
+// else 4; chosen by the planner) per (row, KV head g, split).  A token's K row
+// for head g is head_dim contiguous elements; LPT lanes each load 16 bytes of
+// it, so a wave covers 64/LPT tokens per load instruction (bf16, d=128: 16
+// lanes x 16 B = 256 B per token, 4 tokens per wave).  The G query heads that
+// share KV head g are all served from the same K/V bytes (GQA reuse, fork Q&A
+// Q3 section 2), so every K/V byte is read from HBM once.  One pass: before
+// scoring a round, a lane issues the next round's 16-byte loads (2 K and 2 V,
+// into the second of two register buffers); the scores are summed across the
+// LPT lanes with DPP row operations (bf16 q.k on v_dot2_f32_bf16), and a
+// running max, normaliser and fp32 accumulator per lane group absorb the round
+// (online softmax in the log2 domain).  The groups of a wave and then the
+// waves are combined by log-sum-exp.  Block ids of a split are staged in LDS
+// once.
 //
 // The same kernel also serves as the vector-ALU prefill path: a prefill row is
 // one packed query token whose context is min(q_offset + i + 1, k_len) keys.

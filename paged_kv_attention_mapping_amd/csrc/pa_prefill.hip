@@ -1,5 +1,6 @@
 // pa_prefill.hip -- query-tiled flash-attention prefill over the paged KV
-// cache on bf16 or fp16 MFMA (gfx950), for head_dim 64 and 128.
+// cache on bf16 or fp16 MFMA (gfx950), for head_dim 64, 128 and 256 (256 in
+// the 4-wave layout only), and over INT8 pools at head_dim 64 and 128.
 //
 // What it computes (nano-vllm deep dive, Step 4 path A/B, flash_attn_varlen_func
 // with cu_seqlens and block_table, causal): query i of sequence s sits at
