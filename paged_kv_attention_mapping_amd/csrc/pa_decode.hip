@@ -914,8 +914,9 @@ RowAttnPlan plan_row_attention(int num_rows, const PoolGeom &g, int group, int m
     // Wider workgroups stream one (row, KV head) faster, which shortens the
     // tail when context lengths are ragged; two per CU keep one streaming
     // while the other starts up or reduces.
-    // INT8 pools: 4 waves (the int8 kernel's per-lane state needs about 150
-    // registers; at 8 waves the compiler caps it at 128 and spills).
+    // INT8 pools: 4 waves.  The int8 kernel (about 122 registers) also fits 8
+    // waves, but measured slower on MI355X there: the 256-sequence decode
+    // 125-128 against 112-114 us, the 8 x 512 batch unchanged.
     const int waves = (group <= 2 && g.dtype != 2) ? 8 : 4;
     const int tpr = tokens_per_round(g.dtype, g.d, waves);
     // A split's keys may start anywhere in a block, so it spans at most
